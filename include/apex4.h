@@ -1,0 +1,123 @@
+/*
+ * apex4.h -- C ABI of the MI355X (gfx950) pure W4A4 group-quantized GEMM.
+ *
+ * The operation is the one "APEX4: Efficient Pure W4A4 LLM Inference via
+ * Intra-SM Compute Rebalancing" (aiqbench news page, Abstract) builds its
+ * kernels around: weights and activations both symmetric 4-bit integers with
+ * one scale per row per K-group ("W4A4-g128" for groups of 128), an integer
+ * matrix product per group, and a per-group rescale ("group dequantization")
+ * accumulated in fp32:
+ *
+ *     Y[m,n] = sum_j s_a[m,j] * s_w[n,j] * sum_{k in group j} qa[m,k] * qw[n,k]
+ *
+ * The same page's granularity adaptation makes the group size selectable, and
+ * its mixed-granularity mode is supported as per-channel weight scales
+ * (group_w == K) with grouped activation scales.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers (HIP device memory on the current device)
+ *     unless a comment says otherwise.  Every tensor is row-major and
+ *     contiguous.  The caller owns every buffer; the library allocates nothing,
+ *     frees nothing and keeps no state between calls, so calls are re-entrant.
+ *   - Packed INT4 tensors hold two's-complement 4-bit codes, two per byte, code
+ *     k of a row in byte k/2, the even k in the low nibble.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *     asynchronous and ordered on that stream; results are ready once the
+ *     stream has been synchronized.
+ *   - Arguments are checked on the host before anything is launched.  A
+ *     failed check returns a status code below and touches no memory.  A
+ *     launch failure returns APEX4_ERR_HIP.  Faults during execution surface at
+ *     the caller's next synchronization.  No C++ exception crosses this ABI.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ */
+#ifndef APEX4_H
+#define APEX4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t apex4_status;
+
+#define APEX4_OK 0
+#define APEX4_ERR_INVALID_ARG 1  /* a size or pointer is out of the documented range */
+#define APEX4_ERR_UNSUPPORTED 2  /* a group-size combination this build does not run */
+#define APEX4_ERR_ALIGNMENT 3    /* a pointer lacks the documented alignment */
+#define APEX4_ERR_WORKSPACE 4    /* workspace smaller than apex4_gemm_workspace_size() */
+#define APEX4_ERR_HIP 5          /* the HIP runtime reported an error at launch */
+
+/* Static string naming a status code (host function; never NULL). */
+const char* apex4_status_string(apex4_status s);
+
+/*
+ * Symmetric per-group INT4 quantization of fp16 activations, done online per
+ * token (APEX4 page, Abstract: pure W4A4, activations quantized alongside the
+ * weights).  For each row m and group j (k in [j*g, (j+1)*g)):
+ *     a = max_k |x[m,k]|;  s_a[m,j] = a / 7 (fp32, correctly rounded);
+ *     qa[m,k] = clamp(round_half_even(x[m,k] / s_a[m,j]), -8, 7)
+ *               (fp32 correctly rounded quotient);  a == 0 gives s = 0, q = 0.
+ *   x_f16  [M, K] fp16, 16-byte aligned.
+ *   qa_u8  [M, K/2] packed codes (output), 4-byte aligned.
+ *   s_a    [M, K/group_a] fp32 (output), 4-byte aligned.
+ *   M >= 0 (0 is a no-op), K > 0, K % 8 == 0,
+ *   group_a in {32, 64, 128, 256} or group_a == K, K % group_a == 0.
+ * Output is bit-identical to the reference rule above.
+ */
+apex4_status apex4_quantize_act(const void* x_f16, int64_t M, int64_t K, int32_t group_a,
+                                void* qa_u8, float* s_a, void* stream);
+
+/*
+ * Offline weight packing (APEX4 page, Abstract: the INT4 GEMM consumes INT4
+ * weights): the same per-group rule as apex4_quantize_act, applied to the rows
+ * of W [N, K] (output channels by input features), producing the canonical
+ * packed layout apex4_gemm_w4a4 reads.
+ *   w_f16 [N, K] fp16, 16-byte aligned; qw_u8 [N, K/2]; s_w [N, K/group_w].
+ *   Same size and group rules as apex4_quantize_act (group_w == K gives the
+ *   per-channel scales of the mixed-granularity mode).
+ */
+apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t group_w,
+                               void* qw_u8, float* s_w, void* stream);
+
+/*
+ * Bytes of device workspace apex4_gemm_w4a4 needs for this shape (host
+ * function).  Currently 0 for every shape; callers should still ask.
+ */
+size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a,
+                                 int32_t group_w);
+
+/*
+ * The W4A4 GEMM with per-group dequantization (APEX4 page, Abstract: INT4
+ * products summed per group, each group rescaled and accumulated on the
+ * vector units), Y = X * W^T in the quantized domain:
+ *     P_j[m,n] = sum_{k in group j} qa[m,k] * qw[n,k]          (exact int32)
+ *     Y[m,n]   = sum_j s_a[m, j*gs/group_a] * s_w[n, j*gs/group_w] * P_j[m,n]
+ * with gs = min(group_a, group_w) and G = K/gs groups, accumulated in fp32.
+ * The fp32 summation order is not fixed (the result is within 1e-5 of
+ * max|Y| of the ascending-order sum); P_j is exact.
+ *   qa_u8  [M, K/2] packed, 16-byte aligned;  s_a [M, K/group_a] fp32.
+ *   qw_u8  [N, K/2] packed, 16-byte aligned;  s_w [N, K/group_w] fp32.
+ *   y_f16  [M, N] fp16 output (round to nearest even), 2-byte aligned.
+ *   y_f32  [M, N] fp32 output before the fp16 rounding, or NULL.
+ *   psum_dbg [M, N, G] int32 per-group sums P_j, or NULL (debug; slow).
+ *   workspace / workspace_bytes: at least apex4_gemm_workspace_size() bytes
+ *   (NULL allowed when that is 0).
+ * Sizes: M >= 0, N >= 0 (either 0 is a no-op), K > 0, K % 128 == 0,
+ *   group_a in {32, 64, 128, 256} or group_a == K, and either
+ *   group_w == group_a, or group_w == K (mixed granularity: per-channel
+ *   weights, grouped activations).  M, N, K < 2^31 and M*N*G < 2^31 when
+ *   psum_dbg is given.
+ */
+apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_a,
+                             const void* qw_u8, const float* s_w, int32_t group_w,
+                             int64_t M, int64_t N, int64_t K,
+                             void* y_f16, float* y_f32, int32_t* psum_dbg,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APEX4_H */

@@ -1,0 +1,105 @@
+"""CPU-side checks of the C ABI (include/apex4.h): the library loads, exports
+every declared symbol, and rejects bad arguments on the host with the
+documented status codes.  No call here reaches the GPU: every call fails a
+host-side check, which runs before any HIP call."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from w4a4_group_quantized_amd import apex4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "apex4.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
+A16 = 0x10000          # fake, 16-byte aligned device addresses: never dereferenced
+A16b = 0x20000
+MIS = 0x10001          # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(apex4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(apex4.LIB_PATH):
+        pytest.skip("libapex4.so not built (run __graft_entry__.build())")
+    return apex4.lib()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(apex4.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", apex4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (apex4_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(L):
+    for code in range(6):
+        s = L.apex4_status_string(code)
+        assert s and s.decode() != "unknown status"
+    assert L.apex4_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_size_is_zero(L):
+    assert L.apex4_gemm_workspace_size(2048, 12288, 4096, 128, 128) == 0
+
+
+@pytest.mark.parametrize("fn", ["apex4_quantize_act", "apex4_pack_weight"])
+def test_quantize_validation(L, fn):
+    f = getattr(L, fn)
+    # K not a multiple of 8
+    assert f(A16, 4, 100, 4, A16b, A16b, None) == INVALID
+    # group does not divide K
+    assert f(A16, 4, 1024, 96, A16b, A16b, None) == INVALID
+    # group not in {32,64,128,256,K}
+    assert f(A16, 4, 1024, 16, A16b, A16b, None) == UNSUPPORTED
+    assert f(A16, 4, 1024, 512, A16b, A16b, None) == UNSUPPORTED
+    # negative rows, zero K
+    assert f(A16, -1, 1024, 128, A16b, A16b, None) == INVALID
+    assert f(A16, 4, 0, 128, A16b, A16b, None) == INVALID
+    # null pointers
+    assert f(None, 4, 1024, 128, A16b, A16b, None) == INVALID
+    assert f(A16, 4, 1024, 128, None, A16b, None) == INVALID
+    # misaligned input
+    assert f(MIS, 4, 1024, 128, A16b, A16b, None) == ALIGN
+    assert f(A16, 4, 1024, 128, A16b, A16b + 2, None) == ALIGN
+    # empty input: a successful no-op that touches nothing
+    assert f(None, 0, 1024, 128, None, None, None) == OK
+
+
+def _gemm(L, qa=A16, sa=A16b, ga=128, qw=A16, sw=A16b, gw=128, M=16, N=16, K=1024,
+          y16=A16b, y32=None, ps=None, ws=None, wsb=0):
+    return L.apex4_gemm_w4a4(qa, sa, ga, qw, sw, gw, M, N, K, y16, y32, ps, ws, wsb, None)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, K=1000) == INVALID                 # K % 128
+    assert _gemm(L, K=0) == INVALID
+    assert _gemm(L, M=-1) == INVALID
+    assert _gemm(L, ga=96, gw=96) == INVALID           # does not divide K
+    assert _gemm(L, ga=512, gw=512) == UNSUPPORTED     # not in {32..256, K}
+    assert _gemm(L, ga=128, gw=64) == UNSUPPORTED      # neither equal nor mixed
+    assert _gemm(L, ga=1024, gw=128) == UNSUPPORTED    # converse of mixed mode
+    assert _gemm(L, qa=None) == INVALID
+    assert _gemm(L, y16=None) == INVALID
+    assert _gemm(L, qa=MIS) == ALIGN
+    assert _gemm(L, qw=A16 + 8) == ALIGN
+    assert _gemm(L, y16=A16b + 1) == ALIGN
+    assert _gemm(L, y32=A16b + 2) == ALIGN
+    # psum too large for 32-bit indexing
+    assert _gemm(L, M=65536, N=65536, ps=A16b) == INVALID
+    # empty shapes are successful no-ops
+    assert _gemm(L, M=0, qa=None, sa=None, y16=None) == OK
+    assert _gemm(L, N=0, qw=None, sw=None, y16=None) == OK

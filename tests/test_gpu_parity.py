@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed codes, scales and per-group int32 sums bit-exact; fp32 output
+within 1e-5 of max|Y_ref| (the fp32 summation order on the GPU is free); fp16
+output within one fp16 ulp of fp16(Y_ref).  Small shapes are compared in full;
+the full-size workloads (7B/70B-shaped prefill layers, 70B decode shapes, the
+granularity sweep) are compared on sampled rows (every output row is
+independent) with quantization checked on every row.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import oracle as orc  # noqa: E402
+from w4a4_group_quantized_amd import apex4, inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+REL_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    apex4.lib()   # raises when the HIP library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def check_y(y32, y16, r32):
+    """fp32 within REL_TOL of max|ref|; fp16 within one ulp of fp16(ref)."""
+    scale = float(np.abs(r32).max())
+    err = float(np.abs(y32.astype(np.float64) - r32.astype(np.float64)).max())
+    assert err <= REL_TOL * max(scale, 1e-30), (err, scale)
+    r16 = r32.astype(np.float16)
+    ulp = np.spacing(np.abs(r16)).astype(np.float64)
+    d16 = np.abs(y16.astype(np.float64) - r16.astype(np.float64))
+    assert np.all(d16 <= ulp), float((d16 / ulp).max())
+    return err / max(scale, 1e-30)
+
+
+def gpu_quantize(x, g, dev, weight=False):
+    fn = apex4.pack_weight if weight else apex4.quantize_act
+    q, s = fn(to_dev(x, dev), g)
+    torch.cuda.synchronize()
+    return q, s
+
+
+def run_case(dev, x, w, ga, gw, rows=None, want_p=False):
+    """Quantize X and pack W on the GPU, run the GEMM, compare everything."""
+    M, K = x.shape
+    tqa, tsa = gpu_quantize(x, ga, dev)
+    tqw, tsw = gpu_quantize(w, gw, dev, weight=True)
+    oqa, osa = orc.quantize(x, ga)
+    oqw, osw = orc.quantize(w, gw)
+    assert np.array_equal(tqa.cpu().numpy(), oqa)
+    assert np.array_equal(tsa.cpu().numpy().view(np.uint32), osa.view(np.uint32))
+    assert np.array_equal(tqw.cpu().numpy(), oqw)
+    assert np.array_equal(tsw.cpu().numpy().view(np.uint32), osw.view(np.uint32))
+    y16, y32, ps = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True, want_psum=want_p)
+    torch.cuda.synchronize()
+    r = np.arange(M) if rows is None else rows
+    o16, o32, op = orc.gemm(oqa[r], osa[r], ga, oqw, osw, gw, K, want_p=want_p)
+    rel = check_y(y32.cpu().numpy()[r], y16.cpu().numpy()[r], o32)
+    if want_p:
+        assert np.array_equal(ps.cpu().numpy()[r], op)
+    return rel
+
+
+@functools.lru_cache(maxsize=1)
+def big_problem(M, N, K, act):
+    """Full-size inputs (cached: the sweep's six cases share one draw)."""
+    x, w = inputs.problem(M, N, K, seed=0, act=act)
+    x.setflags(write=False)
+    w.setflags(write=False)
+    return x, w
+
+
+def sample_rows(M, n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    r = set(np.linspace(0, M - 1, n // 2).astype(int).tolist())
+    r |= set(rng.choice(M, size=min(M, n // 2), replace=False).tolist())
+    return np.array(sorted(r))
+
+
+# ------------------------------------------------------------- quantization
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256, "K"])
+@pytest.mark.parametrize("kind", inputs.ACT_KINDS)
+@pytest.mark.parametrize("M,K", [(1, 1024), (37, 1152), (64, 4096)])
+def test_quantize_bitexact(dev, g, kind, M, K):
+    g = K if g == "K" else g
+    if K % g:
+        pytest.skip("group does not divide K")
+    rng = np.random.default_rng(M * 7 + K)
+    x = inputs.activations(rng, M, K, kind, seed=M)
+    x[M // 2, :g] = 0                       # an all-zero group
+    x[0, -8:] = np.float16(3e-7)            # fp16 subnormals
+    q, s = gpu_quantize(x, g, dev)
+    oq, os_ = orc.quantize(x, g)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_quantize_hand_cases_on_gpu(dev):
+    """The hand-worked tie/scale cases in tests/golden, through the GPU kernel."""
+    from tests.test_oracle_pins import _read_quant_cases
+    for c in _read_quant_cases():
+        vals = [float(v) for v in c["x"]]
+        x = np.zeros((1, 32), np.float16)
+        x[0, :len(vals)] = vals
+        q, s = gpu_quantize(x, 32, dev)
+        assert s.cpu().numpy()[0, 0].view(np.uint32) == int(c["scale"][0], 16)
+        codes = orc.codes(q.cpu().numpy(), 32)[0, :len(vals)]
+        assert codes.tolist() == [int(v) for v in c["codes"]]
+
+
+def test_quantize_empty_is_noop(dev):
+    x = torch.empty((0, 256), dtype=torch.float16, device=dev)
+    q, s = apex4.quantize_act(x, 128)
+    assert q.shape == (0, 128) and s.shape == (0, 2)
+
+
+# ------------------------------------------------------------- GEMM, small
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
+def test_gemm_tiny_config(dev, g):
+    """M=16, K=N=1024, X~N(0,1), W~N(0,0.02), seed 0: everything compared, P included."""
+    x, w = inputs.problem(16, 1024, 1024, seed=0, act="normal")
+    run_case(dev, x, w, g, g, want_p=True)
+
+
+@pytest.mark.parametrize("ga", [32, 64, 128, 256])
+def test_gemm_mixed_mode_small(dev, ga):
+    x, w = inputs.problem(40, 200, 1024, seed=3, act="outlier")
+    run_case(dev, x, w, ga, 1024, want_p=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 8, 256), (3, 130, 384), (129, 129, 1152),
+                                   (200, 77, 512), (130, 260, 2048)])
+@pytest.mark.parametrize("g", [32, 128, "K"])
+def test_gemm_ragged_shapes(dev, M, N, K, g):
+    g = K if g == "K" else g
+    x, w = inputs.problem(M, N, K, seed=M + N, act="normal")
+    run_case(dev, x, w, g, g, want_p=True)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
+def test_gemm_unit_scales_integer_exact(dev, g):
+    """Random packed codes (-8 included), all scales 1: Y is the exact integer matmul."""
+    M, N, K = 70, 150, 1024
+    qa, _ = inputs.random_packed(M, K, 1, seed=21)
+    qw, _ = inputs.random_packed(N, K, 1, seed=22)
+    sa = np.ones((M, K // g), np.float32)
+    sw = np.ones((N, K // g), np.float32)
+    y16, y32, ps = apex4.gemm(to_dev(qa, dev), to_dev(sa, dev), g, to_dev(qw, dev),
+                              to_dev(sw, dev), g, K, want_y32=True, want_psum=True)
+    torch.cuda.synchronize()
+    o16, o32, op = orc.gemm(qa, sa, g, qw, sw, g, K, want_p=True)
+    assert np.array_equal(y32.cpu().numpy(), o32)
+    assert np.array_equal(ps.cpu().numpy(), op)
+    assert np.array_equal(y16.cpu().numpy(), o16)
+
+
+def test_gemm_random_scales_and_codes(dev):
+    """Random packed codes with -8 and wide-ranging scales, mixed and equal modes."""
+    M, N, K = 33, 96, 2048
+    for ga, gw, seed in ((128, 128, 1), (64, 2048, 2), (2048, 2048, 3)):
+        qa, sa = inputs.random_packed(M, K, K // ga, seed=seed, scale_lo=1e-4, scale_hi=10.0)
+        qw, sw = inputs.random_packed(N, K, K // gw, seed=seed + 9, scale_lo=1e-4, scale_hi=10.0)
+        y16, y32, ps = apex4.gemm(to_dev(qa, dev), to_dev(sa, dev), ga, to_dev(qw, dev),
+                                  to_dev(sw, dev), gw, K, want_y32=True, want_psum=True)
+        torch.cuda.synchronize()
+        o16, o32, op = orc.gemm(qa, sa, ga, qw, sw, gw, K, want_p=True)
+        assert np.array_equal(ps.cpu().numpy(), op)
+        check_y(y32.cpu().numpy(), y16.cpu().numpy(), o32)
+
+
+def test_gemm_without_optional_outputs(dev):
+    """y16 alone (no fp32, no debug sums) matches the run with them."""
+    x, w = inputs.problem(64, 256, 1024, seed=4)
+    qa, sa = gpu_quantize(x, 128, dev)
+    qw, sw = gpu_quantize(w, 128, dev, weight=True)
+    a = apex4.gemm(qa, sa, 128, qw, sw, 128, 1024)
+    b, _, _ = apex4.gemm(qa, sa, 128, qw, sw, 128, 1024, want_y32=True, want_psum=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_gemm_empty_shapes(dev):
+    z = torch.empty((0, 64), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((0, 1), dtype=torch.float32, device=dev)
+    qw = torch.zeros((8, 64), dtype=torch.uint8, device=dev)
+    sw = torch.ones((8, 1), dtype=torch.float32, device=dev)
+    y = apex4.gemm(z, s0, 128, qw, sw, 128, 128)
+    assert y.shape == (0, 8)
+
+
+# ------------------------------------------------------------- full-size workloads
+
+
+PREFILL_7B = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
+PREFILL_70B = [(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)]
+DECODE = [(8192, 28672), (28672, 8192)]
+
+
+@pytest.mark.parametrize("K,N", PREFILL_7B)
+def test_full_7b_prefill(dev, K, N):
+    x, w = big_problem(2048, N, K, "outlier")
+    run_case(dev, x, w, 128, 128, rows=sample_rows(2048))
+
+
+@pytest.mark.parametrize("K,N", DECODE)
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_full_decode(dev, M, K, N):
+    x, w = big_problem(M, N, K, "normal")
+    run_case(dev, x, w, 128, 128, rows=None if M <= 16 else sample_rows(M))
+
+
+@pytest.mark.parametrize("K,N", PREFILL_70B)
+def test_full_70b_prefill(dev, K, N):
+    x, w = big_problem(4096, N, K, "outlier")
+    run_case(dev, x, w, 128, 128, rows=sample_rows(4096, n=8))
+
+
+@pytest.mark.parametrize("ga,gw", [(32, 32), (64, 64), (128, 128), (256, 256), (8192, 8192),
+                                   (128, 8192)])
+def test_full_granularity_sweep(dev, ga, gw):
+    x, w = big_problem(8192, 28672, 8192, "student_t")
+    run_case(dev, x, w, ga, gw, rows=sample_rows(8192, n=8))

@@ -1,0 +1,142 @@
+"""Thin ctypes binding of libapex4.so (the C ABI in include/apex4.h).
+
+Argument marshalling only: every step of the W4A4 path runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on the GPU (PyTorch is
+used for device memory and streams); calls go on torch's current stream.
+There is no CPU fallback: without the built library or a GPU tensor these
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libapex4.so")
+
+OK = 0
+STATUS_NAMES = {0: "APEX4_OK", 1: "APEX4_ERR_INVALID_ARG", 2: "APEX4_ERR_UNSUPPORTED",
+                3: "APEX4_ERR_ALIGNMENT", 4: "APEX4_ERR_WORKSPACE", 5: "APEX4_ERR_HIP"}
+
+# name -> (restype, argtypes); mirrors include/apex4.h
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+SIGNATURES = {
+    "apex4_status_string": (ctypes.c_char_p, [_I32]),
+    "apex4_quantize_act": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "apex4_pack_weight": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
+    "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
+                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
+}
+
+_lib = None
+
+
+class Apex4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} "
+                         f"({lib().apex4_status_string(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libapex4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m w4a4_group_quantized_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise Apex4Error(fn, status)
+
+
+def _stream(torch, device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_gpu(t, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def quantize_act(x, group: int, out=None):
+    """x: fp16 [M, K] GPU tensor -> (qa uint8 [M, K/2], s_a float32 [M, K/group])."""
+    import torch
+    _need_gpu(x, "x", torch.float16)
+    M, K = x.shape
+    if out is None:
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        sa = torch.empty((M, K // group if group > 0 else 0), dtype=torch.float32, device=x.device)
+    else:
+        qa, sa = out
+    _check("apex4_quantize_act", lib().apex4_quantize_act(
+        _ptr(x), M, K, group, _ptr(qa), _ptr(sa), _stream(torch, x.device)))
+    return qa, sa
+
+
+def pack_weight(w, group: int):
+    """w: fp16 [N, K] GPU tensor -> (qw uint8 [N, K/2], s_w float32 [N, K/group])."""
+    import torch
+    _need_gpu(w, "w", torch.float16)
+    N, K = w.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    sw = torch.empty((N, K // group if group > 0 else 0), dtype=torch.float32, device=w.device)
+    _check("apex4_pack_weight", lib().apex4_pack_weight(
+        _ptr(w), N, K, group, _ptr(qw), _ptr(sw), _stream(torch, w.device)))
+    return qw, sw
+
+
+def workspace_size(M: int, N: int, K: int, ga: int, gw: int) -> int:
+    return int(lib().apex4_gemm_workspace_size(M, N, K, ga, gw))
+
+
+def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bool = False,
+         want_psum: bool = False, y16=None, y32=None):
+    """Y = W4A4 GEMM with per-group dequantization (include/apex4.h).
+
+    Returns y16 [M, N] fp16, or (y16, y32, psum) when want_y32/want_psum is set
+    (entries not asked for are None).
+    """
+    import torch
+    for t, n in ((qa, "qa"), (qw, "qw")):
+        _need_gpu(t, n, torch.uint8)
+    for t, n in ((sa, "s_a"), (sw, "s_w")):
+        _need_gpu(t, n, torch.float32)
+    M, N = qa.shape[0], qw.shape[0]
+    K = 2 * qa.shape[1] if K is None else K
+    dev = qa.device
+    if y16 is None:
+        y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if want_y32 and y32 is None:
+        y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    psum = None
+    if want_psum:
+        psum = torch.empty((M, N, K // min(ga, gw)), dtype=torch.int32, device=dev)
+    ws_bytes = workspace_size(M, N, K, ga, gw)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    _check("apex4_gemm_w4a4", lib().apex4_gemm_w4a4(
+        _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K,
+        _ptr(y16), _ptr(y32), _ptr(psum), _ptr(ws), ws_bytes, _stream(torch, dev)))
+    if want_y32 or want_psum:
+        return y16, y32, psum
+    return y16

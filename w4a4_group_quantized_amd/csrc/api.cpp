@@ -1,0 +1,107 @@
+// C ABI of libapex4 (include/apex4.h): host-side argument checks, then the
+// launch on the caller's stream.  Every check runs before any HIP call, so a
+// rejected call touches neither the device nor the caller's memory.
+#include "apex4.h"
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool small_group(int64_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+apex4_status check_quantize(const void* x, int64_t rows, int64_t K, int32_t g, const void* q,
+                            const float* s)
+{
+    if (rows < 0 || rows > kMaxDim || K <= 0 || K > kMaxDim || K % 8 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (g <= 0 || K % g != 0) return APEX4_ERR_INVALID_ARG;
+    if (!small_group(g) && g != K) return APEX4_ERR_UNSUPPORTED;
+    if (rows == 0) return APEX4_OK;
+    if (!x || !q || !s) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4)) return APEX4_ERR_ALIGNMENT;
+    return APEX4_OK;
+}
+
+apex4_status to_status(hipError_t e) { return e == hipSuccess ? APEX4_OK : APEX4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* apex4_status_string(apex4_status s)
+{
+    switch (s) {
+    case APEX4_OK: return "ok";
+    case APEX4_ERR_INVALID_ARG: return "invalid argument";
+    case APEX4_ERR_UNSUPPORTED: return "unsupported group-size combination";
+    case APEX4_ERR_ALIGNMENT: return "misaligned pointer";
+    case APEX4_ERR_WORKSPACE: return "workspace too small";
+    case APEX4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+apex4_status apex4_quantize_act(const void* x_f16, int64_t M, int64_t K, int32_t group_a,
+                                void* qa_u8, float* s_a, void* stream)
+{
+    const apex4_status st = check_quantize(x_f16, M, K, group_a, qa_u8, s_a);
+    if (st != APEX4_OK || M == 0) return st;
+    return to_status(apex4::launch_quantize(x_f16, M, K, group_a, qa_u8, s_a,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t group_w,
+                               void* qw_u8, float* s_w, void* stream)
+{
+    const apex4_status st = check_quantize(w_f16, N, K, group_w, qw_u8, s_w);
+    if (st != APEX4_OK || N == 0) return st;
+    return to_status(apex4::launch_quantize(w_f16, N, K, group_w, qw_u8, s_w,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t apex4_gemm_workspace_size(int64_t, int64_t, int64_t, int32_t, int32_t) { return 0; }
+
+apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_a,
+                             const void* qw_u8, const float* s_w, int32_t group_w, int64_t M,
+                             int64_t N, int64_t K, void* y_f16, float* y_f32, int32_t* psum_dbg,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (!small_group(group_a) && group_a != K) return APEX4_ERR_UNSUPPORTED;
+    if (!(group_w == group_a || group_w == K)) return APEX4_ERR_UNSUPPORTED;
+    const int64_t gs = group_a < group_w ? group_a : group_w;
+    if (psum_dbg && M * N * (K / gs) > kMaxDim) return APEX4_ERR_INVALID_ARG;
+    const size_t need = apex4_gemm_workspace_size(M, N, K, group_a, group_w);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return APEX4_ERR_WORKSPACE;
+    if (M == 0 || N == 0) return APEX4_OK;
+    if (!qa_u8 || !s_a || !qw_u8 || !s_w || !y_f16) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(qa_u8, 16) || !aligned(qw_u8, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) ||
+        !aligned(y_f16, 2) || !aligned(y_f32, 4) || !aligned(psum_dbg, 4))
+        return APEX4_ERR_ALIGNMENT;
+
+    apex4::GemmProblem p;
+    p.qa = static_cast<const uint8_t*>(qa_u8);
+    p.sa = s_a;
+    p.qw = static_cast<const uint8_t*>(qw_u8);
+    p.sw = s_w;
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.ga = group_a;
+    p.gw = group_w;
+    p.y16 = y_f16;
+    p.y32 = y_f32;
+    p.psum = psum_dbg;
+    return to_status(apex4::launch_gemm(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal launchers behind the C ABI in include/apex4.h.  Arguments are
+// already validated by the caller (api.cpp); each returns hipGetLastError()
+// after its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace apex4 {
+
+// Per-group symmetric INT4 quantization of fp16 rows (activations or weights).
+hipError_t launch_quantize(const void* x_f16, int64_t rows, int64_t K, int32_t g,
+                           void* q_u8, float* s, hipStream_t stream);
+
+struct GemmProblem {
+    const uint8_t* qa;
+    const float* sa;
+    const uint8_t* qw;
+    const float* sw;
+    int32_t M, N, K;
+    int32_t ga, gw;       // group sizes along K of the two operands
+    void* y16;            // fp16 [M, N]
+    float* y32;           // fp32 [M, N] or null
+    int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace apex4

@@ -1,0 +1,106 @@
+// Symmetric per-group INT4 quantization on gfx950 (activations online, weights
+// offline): the rule of the APEX4 page's pure W4A4 scheme, with the readings
+// spelled out in include/apex4.h.  Memory-bound: 16-byte fp16 loads, one
+// packed 32-bit word (8 codes) per thread, group absmax by cross-lane
+// butterflies.  The scale and every quotient are IEEE fp32 divisions (the
+// library is built with correctly rounded fp32 division) and the rounding is
+// v_rndne_f32, so the codes are bit-identical to the rule.
+#include "internal.h"
+
+namespace apex4 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ inline float absmax8(const half8& h)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf((float)h[i]));
+    return m;
+}
+
+// 8 codes of one group-scale, packed little-nibble-first into one word.
+__device__ inline uint32_t quantize8(const half8& h, float scale, bool nonzero)
+{
+    uint32_t word = 0;
+    if (nonzero) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = rintf((float)h[i] / scale);
+            r = fminf(fmaxf(r, -8.0f), 7.0f);
+            word |= ((uint32_t)(int)r & 0xFu) << (4 * i);
+        }
+    }
+    return word;
+}
+
+// Group sizes 32..256: a group is G/8 consecutive lanes of one wave.
+template <int G>
+__global__ __launch_bounds__(256) void quantize_groups_kernel(const half8* __restrict__ x,
+                                                              int64_t n8,
+                                                              uint32_t* __restrict__ q,
+                                                              float* __restrict__ s)
+{
+    constexpr int TPG = G / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = t < n8;
+    half8 h = {};
+    if (live) h = x[t];
+    float amax = absmax8(h);
+#pragma unroll
+    for (int off = TPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = amax / 7.0f;
+    const bool nz = amax != 0.0f;
+    const uint32_t word = quantize8(h, scale, nz);
+    if (live) {
+        q[t] = word;
+        if ((t % TPG) == 0) s[t / TPG] = nz ? scale : 0.0f;
+    }
+}
+
+// One group per row (per-channel scales, any K % 8 == 0): one block per row.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const half8* __restrict__ x,
+                                                            int64_t k8,
+                                                            uint32_t* __restrict__ q,
+                                                            float* __restrict__ s)
+{
+    __shared__ float part[4];
+    const int64_t row = blockIdx.x;
+    const half8* xr = x + row * k8;
+    float amax = 0.0f;
+    for (int64_t i = threadIdx.x; i < k8; i += 256) amax = fmaxf(amax, absmax8(xr[i]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float scale = amax / 7.0f;
+    const bool nz = amax != 0.0f;
+    uint32_t* qr = q + row * k8;
+    for (int64_t i = threadIdx.x; i < k8; i += 256) qr[i] = quantize8(xr[i], scale, nz);
+    if (threadIdx.x == 0) s[row] = nz ? scale : 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x_f16, int64_t rows, int64_t K, int32_t g, void* q_u8,
+                           float* s, hipStream_t stream)
+{
+    const half8* x = static_cast<const half8*>(x_f16);
+    uint32_t* q = static_cast<uint32_t*>(q_u8);
+    const int64_t n8 = rows * (K / 8);
+    const unsigned blocks = (unsigned)((n8 + 255) / 256);
+    switch (g) {
+    case 32: quantize_groups_kernel<32><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 64: quantize_groups_kernel<64><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 128: quantize_groups_kernel<128><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 256: quantize_groups_kernel<256><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    default:  // g == K, checked by the caller
+        quantize_rows_kernel<<<(unsigned)rows, 256, 0, stream>>>(x, K / 8, q, s);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace apex4
