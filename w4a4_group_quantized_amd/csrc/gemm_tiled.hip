@@ -257,7 +257,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
                 if (m < a.M && n < a.N) {
-                    const float v = MIXED ? acc[mt][nt][r] * swn : acc[mt][nt][r];
+                    float v = MIXED ? acc[mt][nt][r] * swn : acc[mt][nt][r];
+                    // keep the fp32 value as is: without this the multiply and the
+                    // fp16 conversion may fuse into one rounding, and y16 would no
+                    // longer be the fp16 rounding of y32
+                    asm volatile("" : "+v"(v));
                     const int64_t o = (int64_t)m * a.N + n;
                     a.y16[o] = (_Float16)v;
                     if (a.y32) a.y32[o] = v;
