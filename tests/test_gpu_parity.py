@@ -41,10 +41,13 @@ def check_y(y32, y16, r32):
     tol = REL_TOL * max(scale, 1e-30)
     err = float(np.abs(y32.astype(np.float64) - r32.astype(np.float64)).max())
     assert err <= tol, (err, scale)
-    assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16))
-    r16 = r32.astype(np.float16)
-    ulp = np.spacing(np.abs(r16)).astype(np.float64)
-    d16 = np.abs(y16.astype(np.float64) - r16.astype(np.float64))
+    with np.errstate(over="ignore"):
+        assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16))
+        r16 = r32.astype(np.float16)
+    fin = np.isfinite(r16)
+    assert np.array_equal(y16[~fin], r16[~fin])     # overflow to +-inf on both sides
+    ulp = np.spacing(np.abs(r16[fin])).astype(np.float64)
+    d16 = np.abs(y16[fin].astype(np.float64) - r16[fin].astype(np.float64))
     assert np.all(d16 <= ulp + tol), float((d16 / (ulp + tol)).max())
     return err / max(scale, 1e-30)
 
@@ -178,8 +181,8 @@ def test_gemm_random_scales_and_codes(dev):
     """Random packed codes with -8 and wide-ranging scales, mixed and equal modes."""
     M, N, K = 33, 96, 2048
     for ga, gw, seed in ((128, 128, 1), (64, 2048, 2), (2048, 2048, 3)):
-        qa, sa = inputs.random_packed(M, K, K // ga, seed=seed, scale_lo=1e-4, scale_hi=10.0)
-        qw, sw = inputs.random_packed(N, K, K // gw, seed=seed + 9, scale_lo=1e-4, scale_hi=10.0)
+        qa, sa = inputs.random_packed(M, K, K // ga, seed=seed, scale_lo=1e-5, scale_hi=0.05)
+        qw, sw = inputs.random_packed(N, K, K // gw, seed=seed + 9, scale_lo=1e-5, scale_hi=0.05)
         y16, y32, ps = apex4.gemm(to_dev(qa, dev), to_dev(sa, dev), ga, to_dev(qw, dev),
                                   to_dev(sw, dev), gw, K, want_y32=True, want_psum=True)
         torch.cuda.synchronize()
