@@ -1,0 +1,224 @@
+"""Benchmark of the W4A4 group-quantized GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for every layer of the workload, online activation quantization
+(apex4_quantize_act) and the GEMM with per-group dequantization
+(apex4_gemm_w4a4), on weights packed once beforehand (untimed, as weights are
+packed offline).  Inputs sit in HBM before the timed region starts.
+
+The default workload is the LLaMA-2-7B-shaped prefill layer set at M=2048
+tokens with g=128: fused QKV (K=4096, N=12288), O-proj (4096, 4096),
+gate+up (4096, 22016) and down (11008, 4096); activations N(0,1) with 1% fixed
+outlier channels x20, weights N(0, 0.02).  Other workloads (decode, 70B
+prefill, the granularity sweep) are selectable for measurement runs.
+
+Prints ONE JSON line: value = effective TOPS (sum of 2*M*N*K over the step's
+GEMMs / step time), plus a roofline object for the GEMM kernel (int8 MFMA
+peak, or HBM for memory-bound workloads) from HIP events around every GEMM
+launch of the timed region, and the CPU oracle timed on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from w4a4_group_quantized_amd import inputs, roofline as rl  # noqa: E402
+
+METRIC = "W4A4-g128 GEMM effective TOPS (2MNK/s); % INT8 MFMA peak / % HBM BW"
+
+# name -> (description, M, [(K, N)...], g_a, g_w, activation kind)
+WORKLOADS = {
+    "llama2-7b-prefill": ("LLaMA-2-7B-shaped prefill layers (QKV, O, gate+up, down), M=2048, g=128",
+                          2048, [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)],
+                          128, 128, "outlier"),
+    "llama2-70b-prefill": ("LLaMA-2-70B-shaped prefill layers (QKV, O, gate+up, down), M=4096, g=128",
+                           4096, [(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)],
+                           128, 128, "outlier"),
+    "sweep-g32": ("granularity sweep M=8192 K=8192 N=28672, g=32", 8192, [(8192, 28672)], 32, 32,
+                  "student_t"),
+    "sweep-g64": ("granularity sweep, g=64", 8192, [(8192, 28672)], 64, 64, "student_t"),
+    "sweep-g128": ("granularity sweep, g=128", 8192, [(8192, 28672)], 128, 128, "student_t"),
+    "sweep-g256": ("granularity sweep, g=256", 8192, [(8192, 28672)], 256, 256, "student_t"),
+    "sweep-gK": ("granularity sweep, g=K=8192 (per-channel)", 8192, [(8192, 28672)], 8192, 8192,
+                 "student_t"),
+    "sweep-mixed": ("granularity sweep, mixed (per-channel weights, g=128 activations)", 8192,
+                    [(8192, 28672)], 128, 8192, "student_t"),
+}
+for _M in (1, 4, 16, 64):
+    WORKLOADS[f"llama2-70b-decode-m{_M}"] = (
+        f"LLaMA-2-70B-shaped decode, M={_M}: up-proj (K=8192, N=28672) and down-proj "
+        f"(K=28672, N=8192), g=128", _M, [(8192, 28672), (28672, 8192)], 128, 128, "normal")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle rows per layer for the CPU baseline (0 = auto, ~10-30 s)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (reference for the HBM "
+                         "byte counters: 1 GiB read + 1 GiB written per launch)")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": dt * 1e3,
+                      "gbs_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def cpu_baseline(layers, M, ga, gw, act, rows_per_layer):
+    """Time the CPU oracle (quantize + GEMM) on the first rows of every layer."""
+    from oracle import oracle
+
+    o = oracle.default()
+    total_ops, total_s = 0.0, 0.0
+    for (K, N) in layers:
+        x, w = inputs.problem(rows_per_layer, N, K, seed=0, act=act)
+        qw, sw = o.quantize(w, gw)                       # offline on both sides: untimed
+        t0 = time.perf_counter()
+        qa, sa = o.quantize(x, ga)
+        o.gemm(qa, sa, ga, qw, sw, gw, K, want_y32=False)
+        total_s += time.perf_counter() - t0
+        total_ops += rl.gemm_ops(rows_per_layer, N, K)
+    return {
+        "value": total_ops / total_s / 1e12,
+        "unit": "TOPS",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows_per_layer} of {M} rows of every layer (quantize + GEMM, weights "
+                  f"pre-packed), {total_s:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from w4a4_group_quantized_amd import apex4
+
+    desc, M, layers, ga, gw, act = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    apex4.lib()
+
+    # --- resident inputs: fp16 activations per layer, weights packed once ---
+    data = []
+    for (K, N) in layers:
+        x, w = inputs.problem(M, N, K, seed=0, act=act)
+        tx = torch.from_numpy(x).to(dev)
+        qw, sw = apex4.pack_weight(torch.from_numpy(w).to(dev), gw)
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        sa = torch.empty((M, K // ga), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        data.append((K, N, tx, qa, sa, qw, sw, y))
+    torch.cuda.synchronize()
+
+    ops_step = sum(rl.gemm_ops(M, N, K) for (K, N) in layers)
+    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) for (K, N) in layers]
+
+    def step(events=None):
+        for li, (K, N, tx, qa, sa, qw, sw, y) in enumerate(data):
+            apex4.quantize_act(tx, ga, out=(qa, sa))
+            if events is not None:
+                events[li][0].record()
+            apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
+            if events is not None:
+                events[li][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, synchronized on both sides; GEMM launches bracketed by events
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    gemm_ms = np.array([[ev[s][li][0].elapsed_time(ev[s][li][1]) for li in range(len(layers))]
+                        for s in range(args.steps)])           # [steps, layers]
+    gemm_ms_avg = gemm_ms.mean(axis=0)
+    layer_ops = np.array([rl.gemm_ops(M, N, K) for (K, N) in layers])
+    bound = rl.bound_of(M, layers[0][1], layers[0][0], ga, gw)
+    if bound == "mfma":
+        achieved = float(layer_ops.sum() / (gemm_ms_avg.sum() * 1e-3)) / 1e12
+        peak = rl.PEAK_INT8_OPS / 1e12
+        unit = "TFLOP/s"
+    else:
+        achieved = float(np.sum(bytes_gemm) / (gemm_ms_avg.sum() * 1e-3)) / 1e9
+        peak = rl.PEAK_HBM_BYTES / 1e9
+        unit = "GB/s"
+
+    per_layer = [{"K": K, "N": N, "gemm_us": round(float(t) * 1e3, 2),
+                  "gemm_tops": round(float(o / (t * 1e-3)) / 1e12, 1),
+                  "gemm_hbm_gbs": round(float(b / (t * 1e-3)) / 1e9, 1)}
+                 for (K, N), t, o, b in zip(layers, gemm_ms_avg, layer_ops, bytes_gemm)]
+    print(json.dumps({"workload": args.workload, "per_layer": per_layer}), file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or min(M, 256)
+        cpu = cpu_baseline(layers, M, ga, gw, act, rows)
+
+    out = {
+        "metric": METRIC,
+        "value": ops_step / (ms_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on i8 MFMA (i32 sums), f32 rescale",
+        "data": "synthetic",
+        "config": {"workload": desc, "M": M, "layers_KN": layers, "group_a": ga, "group_w": gw,
+                   "activations": act, "timed": "quantize_act + gemm per layer",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "gemm (apex4_gemm_w4a4)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,10 +1,11 @@
-// W4A4 GEMM with per-group dequantization on gfx950 (CDNA4).
+// W4A4 GEMM with per-group dequantization on gfx950 (CDNA4): the tiled kernel
+// for row counts where the product is compute-bound (prefill-shaped calls).
 //
 // The computation is the APEX4 page's (Abstract): INT4 x INT4 products summed
 // exactly per K-group on the matrix units, then every group's integer sum is
 // rescaled by s_a*s_w and accumulated in fp32 on the vector ALUs.  gfx950 has
-// no INT4 matrix instruction, so each nibble is widened to an int8 in
-// registers and fed to v_mfma_i32_32x32x32_i8.
+// no INT4 matrix instruction, so each nibble is widened to an int8 and fed to
+// v_mfma_i32_32x32x32_i8.
 //
 // Nibble widening.  A packed word holds 8 codes c0..c7 (c_i in bits 4i..4i+3).
 // (w << 4) & 0xF0F0F0F0 puts c0,c2,c4,c6 in the high half of four bytes and
@@ -13,17 +14,19 @@
 // operands are widened the same way, so the MFMA returns 256*P exactly
 // (|256*P| <= 256*64*K < 2^31 for K < 2^17) and the factor 2^-8 is folded into
 // the activation scale, which is exact.  The even/odd split permutes K inside
-// each 32-value step identically for both operands, so every step still sums
-// exactly the products of one group.
+// each 16-value half of a 32-value step identically for both operands, so
+// every step still sums exactly the products of one group.
 //
-// Tiling.  A workgroup of 4 waves computes a 128x128 tile of Y; each wave a
+// Work split.  A workgroup of 4 waves computes a 128x128 tile of Y; each wave a
 // 64x64 sub-tile as 2x2 MFMA tiles of 32x32.  K advances in stages of 128
-// values (64 packed bytes per row); a stage of A and B is staged through LDS
-// (double-buffered, one barrier per stage) with 16-byte global loads.  Rows of
-// a stage sit 80 bytes apart in LDS so the 16-byte fragment reads of 16
-// consecutive rows cover all banks once.  Inside a row the two 8-byte halves of
-// K-step s are placed so that one 16-byte read gives a lane its half of two
-// consecutive K-steps.
+// values.  The widening is done once per workgroup, in the copy from global
+// memory to LDS: the vector ALUs are the bottleneck of this method, and doing
+// it there instead of after every wave's LDS read halves that work.  A stage
+// of A and B is thus held in LDS as int8 (128 bytes per row, rows 144 bytes
+// apart so that the 16-byte fragment reads of 16 consecutive rows hit every
+// bank once), double-buffered with one barrier per stage; the packed bytes of
+// the next stage are fetched into registers (16-byte global loads) while the
+// current one is multiplied.
 //
 // Rescale cadence follows the group size gs = min(g_a, g_w): after every
 // K-step (gs = 32), every second step (64), or every gs/128 stages (>= 128).
@@ -40,7 +43,7 @@ constexpr int BM = 128;
 constexpr int BN = 128;
 constexpr int KSTAGE = 128;          // K values per stage
 constexpr int ROWB = KSTAGE / 2;     // packed bytes per row per stage
-constexpr int LDS_STRIDE = 80;       // LDS bytes per row (64 + 16 padding)
+constexpr int LDS_STRIDE = 144;      // LDS bytes per row: 128 int8 + 16 padding
 constexpr int MAX_SUB = KSTAGE / 32; // scale groups per stage at gs = 32
 
 struct TileArgs {
@@ -57,14 +60,17 @@ struct TileArgs {
     int32_t* psum;
 };
 
-__device__ inline v4i widen(uint32_t w0, uint32_t w1)
+__device__ inline uint4 widen_lo(uint4 w)
 {
-    v4i r;
-    r[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-    r[1] = (int)(w0 & 0xF0F0F0F0u);
-    r[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-    r[3] = (int)(w1 & 0xF0F0F0F0u);
-    return r;
+    // the first 16 codes of a 32-code chunk (words w.x, w.y) as 16 int8 (x16)
+    return make_uint4((w.x << 4) & 0xF0F0F0F0u, w.x & 0xF0F0F0F0u,
+                      (w.y << 4) & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u);
+}
+
+__device__ inline uint4 widen_hi(uint4 w)
+{
+    return make_uint4((w.z << 4) & 0xF0F0F0F0u, w.z & 0xF0F0F0F0u,
+                      (w.w << 4) & 0xF0F0F0F0u, w.w & 0xF0F0F0F0u);
 }
 
 // Row-in-tile of accumulator register r for this lane (32x32 MFMA output).
@@ -77,8 +83,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) float lds_sa[2][MAX_SUB][BM];
-    __shared__ __attribute__((aligned(16))) float lds_sw[2][MAX_SUB][BN];
+    constexpr int SUBS = GS_STEPS ? MAX_SUB / GS_STEPS : 1;   // scale groups per stage
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][SUBS][BM];
+    __shared__ __attribute__((aligned(16))) float lds_sw[2][MIXED ? 1 : SUBS][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -87,10 +94,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int64_t rowbytes = a.K / 2;
     const int stages = a.K / KSTAGE;
-    const int nsub = GS_STEPS ? MAX_SUB / GS_STEPS : 1;   // scale groups per stage
+    const int nsub = SUBS;
     const int stages_per_group = GS_STEPS ? 1 : a.gs / KSTAGE;
 
-    // --- global -> register staging (2 chunks of A and 2 of B per thread) ---
+    // --- global -> register staging: 2 chunks (16 packed bytes = one K-step
+    // of one row) of A and 2 of B per thread, plus 2 scales of each ---
     uint4 ra[2], rb[2];
     float rsa[2], rsw[2];
 
@@ -98,15 +106,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 256 * i;
-            const int row = c >> 2, ch = c & 3;
-            const int64_t koff = (int64_t)t * ROWB + ch * 16;
+            const int row = c >> 2, s = c & 3;
+            const int64_t koff = (int64_t)t * ROWB + s * 16;
             const int am = m0 + row, bn = n0 + row;
             ra[i] = am < a.M ? *reinterpret_cast<const uint4*>(a.qa + am * rowbytes + koff)
                              : make_uint4(0, 0, 0, 0);
             rb[i] = bn < a.N ? *reinterpret_cast<const uint4*>(a.qw + bn * rowbytes + koff)
                              : make_uint4(0, 0, 0, 0);
         }
-        // scales: nsub groups of this stage, for BM rows of A and BN rows of B
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int idx = tid + 256 * i;
@@ -122,18 +129,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
         }
     };
 
+    // widen the staged chunks and store them: K-step s of a row occupies bytes
+    // [32s, 32s+32) of the row, first half (codes 0..15) then second half
     auto store_stage = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 256 * i;
-            const int row = c >> 2, s = c & 3;           // chunk = K-step s of the stage
-            // half h of step s goes to slot 2*(s/2)+h, at byte 8*(s%2) inside the slot
-            const int o0 = row * LDS_STRIDE + 16 * (2 * (s >> 1) + 0) + 8 * (s & 1);
-            const int o1 = row * LDS_STRIDE + 16 * (2 * (s >> 1) + 1) + 8 * (s & 1);
-            *reinterpret_cast<uint2*>(&lds_a[buf][o0]) = make_uint2(ra[i].x, ra[i].y);
-            *reinterpret_cast<uint2*>(&lds_a[buf][o1]) = make_uint2(ra[i].z, ra[i].w);
-            *reinterpret_cast<uint2*>(&lds_b[buf][o0]) = make_uint2(rb[i].x, rb[i].y);
-            *reinterpret_cast<uint2*>(&lds_b[buf][o1]) = make_uint2(rb[i].z, rb[i].w);
+            const int row = c >> 2, s = c & 3;
+            const int o = row * LDS_STRIDE + 32 * s;
+            *reinterpret_cast<uint4*>(&lds_a[buf][o]) = widen_lo(ra[i]);
+            *reinterpret_cast<uint4*>(&lds_a[buf][o + 16]) = widen_hi(ra[i]);
+            *reinterpret_cast<uint4*>(&lds_b[buf][o]) = widen_lo(rb[i]);
+            *reinterpret_cast<uint4*>(&lds_b[buf][o + 16]) = widen_hi(rb[i]);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -154,11 +161,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
         for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
-            P[mt][nt] = v16i{};
         }
 
     // Rescale the finished group held in P (scale-group `sub` of stage buffer
-    // `buf`, global group index j) into acc, then clear P.
+    // `buf`, global group index j) into acc.
     auto rescale = [&](int buf, int sub, int j) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -190,7 +196,6 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
                             a.psum[((int64_t)m * a.N + n) * a.G + j] = P[mt][nt][r] >> 8;
                     }
                 }
-                P[mt][nt] = v16i{};
             }
         }
     };
@@ -203,41 +208,39 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(TileArgs a)
         const int buf = t & 1;
         if (t + 1 < stages) load_stage(t + 1);
 
-        const uint8_t* la = lds_a[buf];
-        const uint8_t* lb = lds_b[buf];
-        // small groups rescale inside this loop; keeping it rolled keeps the
-        // fragments of only one step pair live across a rescale
-#pragma unroll (GS_STEPS ? 1 : 2)
-        for (int c = 0; c < 2; ++c) {
-            v4i fa[2][2], fb[2][2];   // [tile][step in pair]
+        const uint8_t* la = lds_a[buf] + (wm * 64 + (lane & 31)) * LDS_STRIDE + 16 * (lane >> 5);
+        const uint8_t* lb = lds_b[buf] + (wn * 64 + (lane & 31)) * LDS_STRIDE + 16 * (lane >> 5);
+        // small groups rescale inside this loop; keeping it rolled there keeps
+        // the fragments of only one step live across a rescale
+#pragma unroll (GS_STEPS ? 1 : 4)
+        for (int s = 0; s < 4; ++s) {
+            v4i fa[2], fb[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int row = wm * 64 + mt * 32 + (lane & 31);
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    la + row * LDS_STRIDE + 16 * (2 * c + (lane >> 5)));
-                fa[mt][0] = widen(v.x, v.y);
-                fa[mt][1] = widen(v.z, v.w);
-            }
+            for (int mt = 0; mt < 2; ++mt)
+                fa[mt] = *reinterpret_cast<const v4i*>(la + mt * 32 * LDS_STRIDE + 32 * s);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int row = wn * 64 + nt * 32 + (lane & 31);
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    lb + row * LDS_STRIDE + 16 * (2 * c + (lane >> 5)));
-                fb[nt][0] = widen(v.x, v.y);
-                fb[nt][1] = widen(v.z, v.w);
-            }
-#pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
+            for (int nt = 0; nt < 2; ++nt)
+                fb[nt] = *reinterpret_cast<const v4i*>(lb + nt * 32 * LDS_STRIDE + 32 * s);
+            // the first K-step of a group starts from a zero accumulator (an
+            // inline constant), so no registers are spent clearing P
+            const bool first = GS_STEPS ? (s % GS_STEPS == 0) : (s == 0 && t % stages_per_group == 0);
+            if (first) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-                        P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][ss], fb[nt][ss],
-                                                                         P[mt][nt], 0, 0, 0);
-                const int step = 2 * c + ss;
-                if (GS_STEPS == 1) rescale(buf, step, t * MAX_SUB + step);
-                if (GS_STEPS == 2 && ss == 1) rescale(buf, c, t * (MAX_SUB / 2) + c);
+                        P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt], fb[nt], v16i{},
+                                                                         0, 0, 0);
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt], fb[nt], P[mt][nt],
+                                                                         0, 0, 0);
             }
+            if (GS_STEPS == 1) rescale(buf, s, t * MAX_SUB + s);
+            if (GS_STEPS == 2 && (s & 1)) rescale(buf, s >> 1, t * (MAX_SUB / 2) + (s >> 1));
         }
         if (GS_STEPS == 0 && (t + 1) % stages_per_group == 0) rescale(buf, 0, t / stages_per_group);
 
@@ -286,7 +289,7 @@ void launch_tiled_mode(const TileArgs& t, bool mixed, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
+hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream)
 {
     TileArgs t;
     t.qa = p.qa;

@@ -23,6 +23,12 @@ struct GemmProblem {
     int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
 };
 
+// Picks the kernel for the shape: the skinny kernel (streams the weights; few
+// rows, groups >= 128) or the tiled kernel (everything else).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
+bool skinny_supports(const GemmProblem& p);
+hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace apex4
