@@ -12,7 +12,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libapex4.so")
+# APEX4_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("APEX4_LIB", os.path.join(PKG, "libapex4.so"))
 
 OK = 0
 STATUS_NAMES = {0: "APEX4_OK", 1: "APEX4_ERR_INVALID_ARG", 2: "APEX4_ERR_UNSUPPORTED",

@@ -32,13 +32,16 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str | None = None, defines: tuple = ()) -> str:
+    """Compile every source and link libapex4.so (or `out`, with extra -D defines)."""
     objs = []
-    bdir = os.path.join(PKG, "_build")
+    lib = out or LIB
+    bdir = os.path.join(os.path.dirname(lib), "_build")
     os.makedirs(bdir, exist_ok=True)
     for src in sources():
         obj = os.path.join(bdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC,
+               "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,10 +53,10 @@ def build(verbose: bool = False) -> str:
         if msg.strip() and verbose:
             print(msg)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
