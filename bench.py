@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="oracle rows per layer for the CPU baseline (0 = auto, ~10-30 s)")
+                    help="oracle rows per layer for the CPU baseline (0 = sized for ~12 s)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (reference for the HBM "
                          "byte counters: 1 GiB read + 1 GiB written per launch)")
@@ -91,11 +91,26 @@ def calibrate_copy():
                       "gbs_read_plus_write": 2 * n / dt / 1e9}))
 
 
-def cpu_baseline(layers, M, ga, gw, act, rows_per_layer):
-    """Time the CPU oracle (quantize + GEMM) on the first rows of every layer."""
+def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
+    """Time the CPU oracle (quantize + GEMM) on the first rows of every layer.
+
+    rows_per_layer = 0 sizes the sample from a 4-row trial so the timed work
+    takes about target_s seconds.
+    """
     from oracle import oracle
 
     o = oracle.default()
+    if rows_per_layer <= 0:
+        trial = 4
+        t = 0.0
+        for (K, N) in layers:
+            x, w = inputs.problem(trial, N, K, seed=0, act=act)
+            qw, sw = o.quantize(w, gw)
+            t0 = time.perf_counter()
+            qa, sa = o.quantize(x, ga)
+            o.gemm(qa, sa, ga, qw, sw, gw, K, want_y32=False)
+            t += time.perf_counter() - t0
+        rows_per_layer = int(max(trial, min(M, trial * target_s / max(t, 1e-6))))
     total_ops, total_s = 0.0, 0.0
     for (K, N) in layers:
         x, w = inputs.problem(rows_per_layer, N, K, seed=0, act=act)
@@ -113,6 +128,24 @@ def cpu_baseline(layers, M, ga, gw, act, rows_per_layer):
         "sample": f"first {rows_per_layer} of {M} rows of every layer (quantize + GEMM, weights "
                   f"pre-packed), {total_s:.1f} s",
     }
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counters
+    (profiles/hbm_traffic.json), or None when that workload was not counted
+    or its kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["workloads"][workload]
+        src = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc", rec["kernel_source"])
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+                return None
+        return rec["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -201,8 +234,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or min(M, 256)
-        cpu = cpu_baseline(layers, M, ga, gw, act, rows)
+        cpu = cpu_baseline(layers, M, ga, gw, act, args.cpu_rows)
 
     out = {
         "metric": METRIC,
@@ -222,7 +254,8 @@ def main():
                    "weight_copies_cycled": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": measured_traffic(args.workload),
+                     "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
                      "kernel": "gemm (apex4_gemm_w4a4)"},
         "cpu_baseline": cpu,
     }
