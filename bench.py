@@ -73,6 +73,11 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (reference for the HBM "
                          "byte counters: 1 GiB read + 1 GiB written per launch)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
+                         "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-decode-m16",
+                    help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
 
@@ -130,26 +135,95 @@ def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
     }
 
 
-def measured_traffic(workload):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counters
-    (profiles/hbm_traffic.json), or None when that workload was not counted
-    or its kernel source changed since."""
+def kernel_sources_sha256():
+    """sha256 over the library's kernel sources (every file name and content
+    under w4a4_group_quantized_amd/csrc, in name order)."""
     import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Mean HBM bytes per GEMM launch from the committed rocprofv3 counters
+    (profiles/hbm_traffic.json), or None when that workload was not counted
+    or the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)["workloads"][workload]
-        src = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc", rec["kernel_source"])
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-                return None
+        if rec["kernel_sources_sha256"] != kernel_sources_sha256():
+            return None
         return rec["hbm_bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
 
 
+def write_traffic(prof_dir, workloads):
+    """Write profiles/hbm_traffic.json from rocprofv3 counter runs.
+
+    Expects <prof_dir>/pmc_<C>_<name>/run_counter_collection.csv for C in
+    FETCH_SIZE, WRITE_SIZE and name in copy (python bench.py --calibrate-copy)
+    and each workload (python bench.py --workload W --no-cpu-baseline).  Each
+    counter is scaled by the factor that makes it read 1 GiB for the 1 GiB
+    copy; the GEMM dispatches of a workload cycle through its layers in order.
+    """
+    import csv
+
+    def rows(counter, name):
+        path = os.path.join(prof_dir, f"pmc_{counter}_{name}", "run_counter_collection.csv")
+        with open(path) as f:
+            r = list(csv.DictReader(f))
+        return sorted((int(x["Dispatch_Id"]), x["Kernel_Name"], float(x["Counter_Value"])) for x in r)
+
+    def copies(counter):
+        v = [val for _, k, val in rows(counter, "copy") if "copyBuffer" in k]
+        return sum(v) / len(v)
+
+    gib_kib = float(1 << 20)
+    cal = {"copy_fetch_kib_per_GiB": copies("FETCH_SIZE"), "copy_write_kib_per_GiB": copies("WRITE_SIZE")}
+    cal["fetch_factor"] = gib_kib / cal["copy_fetch_kib_per_GiB"]
+    cal["write_factor"] = gib_kib / cal["copy_write_kib_per_GiB"]
+    out = {"description": "HBM bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                          "(KiB per dispatch), each scaled by the factor that makes the same counter read "
+                          "1 GiB for a plain 1 GiB device copy; written by python bench.py --write-traffic. "
+                          "bench.py reports them only while the kernel sources hash the same.",
+           "calibration": cal, "workloads": {}}
+    sha = kernel_sources_sha256()
+    for wl in workloads:
+        _, M, layers, ga, gw, _ = WORKLOADS[wl]
+        gemm = lambda c: [v for _, k, v in rows(c, wl) if "gemm" in k and "quantize" not in k]
+        fr, wr = gemm("FETCH_SIZE"), gemm("WRITE_SIZE")
+        per = []
+        for li, (K, N) in enumerate(layers):
+            f = fr[li::len(layers)]
+            w = wr[li::len(layers)]
+            per.append({"M": M, "K": K, "N": N, "dispatches": len(f),
+                        "fetch_bytes": sum(f) / len(f) * 1024 * cal["fetch_factor"],
+                        "write_bytes": sum(w) / len(w) * 1024 * cal["write_factor"],
+                        "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw)})
+        out["workloads"][wl] = {
+            "kernel_sources_sha256": sha,
+            "hbm_bytes_per_launch": float(np.mean([p["fetch_bytes"] + p["write_bytes"] for p in per])),
+            "algorithmic_bytes_per_launch": float(np.mean([p["algorithmic_bytes"] for p in per])),
+            "per_layer": per,
+        }
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({w: out["workloads"][w]["hbm_bytes_per_launch"] for w in workloads}))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.traffic_workloads.split(","))
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return

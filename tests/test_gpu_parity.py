@@ -30,7 +30,7 @@ def dev():
 
 
 def to_dev(a, dev):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return torch.from_numpy(np.array(a, copy=True, order="C")).to(dev)
 
 
 def check_y(y32, y16, r32):
@@ -145,9 +145,12 @@ def test_gemm_tiny_config(dev, g):
     run_case(dev, x, w, g, g, want_p=True)
 
 
+@pytest.mark.parametrize("M", [40, 300])
 @pytest.mark.parametrize("ga", [32, 64, 128, 256])
-def test_gemm_mixed_mode_small(dev, ga):
-    x, w = inputs.problem(40, 200, 1024, seed=3, act="outlier")
+def test_gemm_mixed_mode_small(dev, ga, M):
+    """Per-channel weight scales with grouped activations: 40 rows take the
+    weight-streaming kernel, 300 rows (two row tiles, ragged) a tiled one."""
+    x, w = inputs.problem(M, 200, 1024, seed=3, act="outlier")
     run_case(dev, x, w, ga, 1024, want_p=True)
 
 

@@ -1,0 +1,494 @@
+// W4A4 GEMM with per-group dequantization on gfx950: the ping-pong tiled
+// kernel for compute-bound calls with groups of 128 (or one group over K).
+//
+// The computation is the APEX4 page's (Abstract): INT4 x INT4 products summed
+// exactly per K-group on the matrix units, every group's integer sum rescaled
+// by s_a*s_w and accumulated in fp32 on the vector ALUs.  Per 32x32 tile and
+// group of 128 the int8 MFMA is busy 128 cycles and the rescale (convert +
+// fma for 16 outputs per lane) keeps the vector ALU busy about as long, so
+// the two must run at the same time to get near the matrix-unit bound.
+//
+// Ping-pong.  A workgroup of 8 waves computes a 256x128 tile of Y, each wave a
+// 64x64 sub-tile (2x2 MFMA tiles of 32x32x32 int8).  Waves are placed on the
+// four SIMDs of a CU round-robin, so SIMD i holds waves i and i+4.  Waves 0..3
+// run half a K-stage ahead of waves 4..7: between two barriers one wave of
+// every SIMD issues the matrix work of a stage while the other issues the
+// vector rescale of the stage it finished before; at the next barrier the
+// roles swap.  The hardware then keeps both units of the SIMD busy from two
+// instruction streams, which no static schedule of one wave achieved here.
+//
+//   waves 0..3, stage t:  | matrix(t)    | rescale(t)  |
+//   waves 4..7, stage t:  | rescale(t-1) | matrix(t)   |
+//
+// The matrix phase holds everything that needs LDS or the matrix unit: the
+// fragment reads and the 16 int8 MFMAs of the stage, the copy of stage t+1
+// (16-byte global loads two stages ahead, widened to int8 and stored to LDS,
+// interleaved with the MFMAs by the scheduler), and the scale products
+// S = s_a * s_w of the 4 tiles.  The vector phase is only the convert + fma
+// of the 64 outputs per lane, from registers.
+//
+// LDS: A and B stages (int8, widened from nibbles in the global -> LDS copy,
+// 144-byte rows so that 16 consecutive rows hit every bank once) and the
+// scale operands are double-buffered.
+//
+// Nibble widening, the 2^-8 fold, the bf16 split of the scale products and
+// the fixed-order fp32 accumulation are those of the other tiled kernel:
+// (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0 give the int8 values 16*c, the
+// MFMA returns 256*P exactly, and S = (2^-8 s_a) * s_w comes from one bf16
+// MFMA over the exact three-piece splits of both scales (six of the nine cross
+// products; the three dropped are below 2^-23 of S).  One group over all of K
+// (per-channel scales) keeps P in the MFMA accumulator through the loop and
+// is rescaled once.  Mixed mode (per-channel weight scales, activation groups
+// of 128) rescales with s_a alone and applies s_w in the epilogue.
+#include "internal.h"
+
+namespace apex4 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256;
+constexpr int BN = 128;
+constexpr int THREADS = 512;
+constexpr int HALF = THREADS / 2;       // threads per wave group
+constexpr int KSTAGE = 128;             // K values per stage
+constexpr int ROWB = KSTAGE / 2;        // packed bytes per row per stage
+constexpr int STRIDE = 144;             // LDS bytes per int8 row (128 + 16 padding)
+constexpr uint32_t A_BYTES = BM * STRIDE;
+constexpr uint32_t B_BYTES = BN * STRIDE;
+
+struct PPArgs {
+    const uint8_t* qa;
+    const float* sa;
+    const uint8_t* qw;
+    const float* sw;
+    int M, N, K;
+    int Ga, Gw;        // scale columns per row: K/ga, K/gw
+    int spg;           // stages per group: gs / 128 (1, or all of K)
+    int G;             // K / gs
+    _Float16* y16;
+    float* y32;
+    int32_t* psum;
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes)
+{
+    // raw buffer: loads past `bytes` return zeros
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uint4 widen_lo(uint4 w)
+{
+    return make_uint4((w.x << 4) & 0xF0F0F0F0u, w.x & 0xF0F0F0F0u,
+                      (w.y << 4) & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u);
+}
+
+__device__ inline uint4 widen_hi(uint4 w)
+{
+    return make_uint4((w.z << 4) & 0xF0F0F0F0u, w.z & 0xF0F0F0F0u,
+                      (w.w << 4) & 0xF0F0F0F0u, w.w & 0xF0F0F0F0u);
+}
+
+__device__ inline uint32_t bf16_trunc_bits(float x) { return __builtin_bit_cast(uint32_t, x) >> 16; }
+
+// exact split s = x0 + x1 + x2 into bf16 values (truncation at each step)
+__device__ inline void split3(float s, uint32_t& x0, uint32_t& x1, uint32_t& x2)
+{
+    x0 = bf16_trunc_bits(s);
+    const float r1 = s - __builtin_bit_cast(float, x0 << 16);
+    x1 = bf16_trunc_bits(r1);
+    const float r2 = r1 - __builtin_bit_cast(float, x1 << 16);
+    x2 = bf16_trunc_bits(r2);
+}
+
+// Register anchors.  An empty volatile asm that takes a value in and out keeps
+// its producers before and its consumers after this point in program order;
+// volatile asm statements and the barrier keep their relative order.  The
+// arithmetic of each phase stays between its two barriers this way (pure
+// register arithmetic may otherwise be moved across a barrier).
+__device__ inline void anchor(float& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void anchor(int& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void anchor(uint4& x)
+{
+    asm volatile("" : "+v"(x.x));
+    asm volatile("" : "+v"(x.y));
+    asm volatile("" : "+v"(x.z));
+    asm volatile("" : "+v"(x.w));
+}
+
+__device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// LDS of one workgroup
+struct PPShared {
+    uint8_t a[2][A_BYTES];
+    uint8_t b[2][B_BYTES];
+    // Scale operands, per stage buffer: one 32-byte row per tile row, the bf16
+    // pieces in slots 0..5 and zeros in slots 6..15 (lanes 32..63 of the
+    // split-operand MFMA read the upper, zero half), or in mixed mode fp32
+    // 2^-8 s_a in the first BM dwords of ta.
+    uint4 ta[2][BM][2];
+    uint4 tb[2][BN][2];
+};
+
+// Orders this wave's LDS accesses around the workgroup barrier (LDS only:
+// global loads in flight stay in flight).
+// The scheduling fences keep every instruction on its side of the barrier.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// SPG: stages per group, 1 (g = 128) or 0 (one group, g = K).  EARLY: this
+// wave belongs to waves 0..3.
+template <bool MIXED, bool DEBUG_P, int SPG, bool EARLY>
+__device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;      // 64-row, 64-column sub-tile
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const uint32_t rowbytes = (uint32_t)a.K / 2;
+    const int stages = a.K / KSTAGE;
+    const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
+    // Per-workgroup buffers: rows past M (N) lie past the end and read zeros.
+    // The per-stage offset goes into the scalar offset of the load.
+    const __amdgpu_buffer_rsrc_t rA = buffer_of(a.qa + (int64_t)m0 * rowbytes, (uint32_t)rows_a * rowbytes);
+    const __amdgpu_buffer_rsrc_t rB = buffer_of(a.qw + (int64_t)n0 * rowbytes, (uint32_t)rows_b * rowbytes);
+    const __amdgpu_buffer_rsrc_t rSA = buffer_of(a.sa + (int64_t)m0 * a.Ga, (uint32_t)rows_a * a.Ga * 4);
+    const __amdgpu_buffer_rsrc_t rSW = buffer_of(a.sw + (int64_t)n0 * a.Gw, (uint32_t)rows_b * a.Gw * 4);
+
+    // --- this thread's share of a stage copy: 3 chunks of 16 packed bytes
+    // (one 32-code K-step of a row).  Waves 0..3: A rows 0..191 and the A
+    // scales; waves 4..7: A rows 192..255, all of B and the B scales. ---
+    const int ht = EARLY ? tid : tid - HALF;
+    uint32_t goff[3], loff[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        int c;
+        if (EARLY) c = ht + HALF * j;                      // A chunks 0..767
+        else c = j == 0 ? 3 * HALF + ht : ht + HALF * (j - 1);   // A 768..1023; B 0..511
+        const int row = c >> 2, s = c & 3;
+        goff[j] = (uint32_t)row * rowbytes + 16 * s;
+        loff[j] = row * STRIDE + 32 * s;
+    }
+    // chunk j's operand: A, or B for chunks 1 and 2 of waves 4..7
+    auto chunk_is_b = [](int j) { return !EARLY && j > 0; };
+    const bool has_scale = EARLY ? true : (!MIXED && ht < BN);
+    // threads without a scale row load from past the end (zeros), so that
+    // every load is unconditional and the wait counts stay exact
+    const uint32_t soff = !has_scale ? 0x80000000u : EARLY ? (uint32_t)ht * a.Ga * 4 : (uint32_t)ht * a.Gw * 4;
+
+    uint4 rq[2][3];
+    float rs[2];
+    auto load_stage = [&](int t, int set) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], t * ROWB, 0);
+            rq[set][j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        // the scale of the group that stage t belongs to
+        const int g = (SPG == 1 ? t : 0) * 4;
+        if (EARLY || !MIXED)
+            rs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g, 0));
+    };
+    auto store_stage = [&](int buf, int set) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) anchor(rq[set][j]);   // widen in this phase
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            uint8_t* base = chunk_is_b(j) ? sh.b[buf] : sh.a[buf];
+            *reinterpret_cast<uint4*>(base + loff[j]) = widen_lo(rq[set][j]);
+            *reinterpret_cast<uint4*>(base + loff[j] + 16) = widen_hi(rq[set][j]);
+        }
+        if (EARLY) {
+            // A scale of row ht, with the 2^-8 of the widened operands folded in
+            const float s = rs[set] * 0.00390625f;
+            if (MIXED) {
+                reinterpret_cast<float*>(sh.ta[buf])[ht] = s;
+            } else {
+                uint32_t x0, x1, x2;
+                split3(s, x0, x1, x2);
+                // slots 0..5: x0 x0 x0 x1 x1 x2 (paired with y0 y1 y2 y0 y1 y0)
+                sh.ta[buf][ht][0] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
+            }
+        } else if (has_scale) {
+            uint32_t y0, y1, y2;
+            split3(rs[set], y0, y1, y2);
+            sh.tb[buf][ht][0] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+        }
+    };
+
+    float acc[2][2][16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
+    v16i P[2][2];
+    v16f S[2][2];   // scale products of the group in P
+    if (SPG == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) P[mt][nt] = v16i{};
+    }
+
+    const uint32_t frag = (wm * 64 + (lane & 31)) * STRIDE + 16 * (lane >> 5);
+    const uint32_t fragb = (wn * 64 + (lane & 31)) * STRIDE + 16 * (lane >> 5);
+    const int trow = lane & 31, thalf = lane >> 5;
+    // The scale products S of the 4 tiles for the group of stage buffer `buf`,
+    // on the matrix unit, so that the vector phase has no LDS or matrix-unit
+    // dependency.
+    auto scale_products = [&](int buf) {
+        if (MIXED) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float* sp = reinterpret_cast<const float*>(sh.ta[buf]) + wm * 64 + mt * 32 + 4 * thalf;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(sp + 8 * q);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        S[mt][nt][4 * q + 0] = v.x;
+                        S[mt][nt][4 * q + 1] = v.y;
+                        S[mt][nt][4 * q + 2] = v.z;
+                        S[mt][nt][4 * q + 3] = v.w;
+                    }
+                }
+            }
+        } else {
+            v8bf opa[2], opb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                opa[i] = __builtin_bit_cast(v8bf, sh.ta[buf][wm * 64 + i * 32 + trow][thalf]);
+                opb[i] = __builtin_bit_cast(v8bf, sh.tb[buf][wn * 64 + i * 32 + trow][thalf]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[mt], opb[nt], v16f{}, 0, 0, 0);
+        }
+    };
+    // Matrix phase of stage buffer `buf`: the 16 int8 MFMAs, K-step-major so
+    // that consecutive MFMAs are independent (`zero`: the stage starts a group
+    // and the MFMAs start from zero), then, when the stage ends a group
+    // (`ends`), the scale products.
+    auto mma_stage = [&](int buf, bool zero, bool ends) {
+        const uint8_t* la = sh.a[buf] + frag;
+        const uint8_t* lb = sh.b[buf] + fragb;
+        v4i fa[2][4], fb[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
+                fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
+            }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][0], fb[nt][0], zero ? v16i{} : P[mt][nt], 0, 0, 0);
+#pragma unroll
+        for (int s = 1; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][s], fb[nt][s], P[mt][nt], 0, 0, 0);
+        if (ends) scale_products(buf);
+    };
+
+    // Vector phase: acc += S (.) P for the finished group j.  The anchors
+    // keep the conversion and the updates between this phase's barriers.
+    auto rescale = [&](int j) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    int x = P[mt][nt][r];
+                    anchor(x);
+                    P[mt][nt][r] = x;
+                    float y = S[mt][nt][r];
+                    anchor(y);
+                    S[mt][nt][r] = y;
+                }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[mt][nt][r] = fmaf(S[mt][nt][r], (float)P[mt][nt][r], acc[mt][nt][r]);
+                if (DEBUG_P) {
+                    const int n = n0 + wn * 64 + nt * 32 + (lane & 31);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
+                        if (m < a.M && n < a.N) a.psum[((int64_t)m * a.N + n) * a.G + j] = P[mt][nt][r] >> 8;
+                    }
+                }
+            }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) anchor(acc[mt][nt][r]);
+    };
+
+    // --- prologue: the zero halves of the scale rows, stages 0 and 1 in
+    // flight, stage 0 into buffer 0 ---
+    if (!MIXED) {
+        for (int i = tid; i < 2 * (BM + BN); i += THREADS) {
+            uint4* row = i < 2 * BM ? sh.ta[i / BM][i % BM] : sh.tb[(i - 2 * BM) / BN][(i - 2 * BM) % BN];
+            row[1] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    load_stage(0, 0);
+    load_stage(1, 1);
+    store_stage(0, 0);
+    lds_barrier();
+
+    // Stage t uses A/B and scale buffer t&1 and register set t&1; the loop is
+    // unrolled by two so that these are compile-time indices.
+    for (int t0 = 0; t0 < stages; t0 += 2)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int t = t0 + h;
+        if (t >= stages) break;
+        constexpr bool zero = SPG == 1;   // stage t starts a group
+        constexpr bool ends = SPG == 1;   // stage t ends a group
+        // The copy runs in every stage, also past the last one: loads past the
+        // end of K read other rows or zeros, and the stores go to a buffer
+        // that is no longer read; unconditional memory operations keep the
+        // wait counts exact (the loads of stage t+2 stay in flight).
+        if (EARLY) {
+            // phase 1: matrix work of stage t, copy of stage t+1
+            load_stage(t + 2, h);
+            mma_stage(h, zero, ends);
+            store_stage(h ^ 1, h ^ 1);
+            lds_barrier();
+            // phase 2: rescale of stage t
+            if (ends) rescale(t);
+            lds_barrier();
+        } else {
+            // phase 1: rescale of stage t-1
+            if (ends && t > 0) rescale(t - 1);
+            lds_barrier();
+            // phase 2: matrix work of stage t, copy of stage t+1
+            load_stage(t + 2, h);
+            mma_stage(h, zero, ends);
+            store_stage(h ^ 1, h ^ 1);
+            lds_barrier();
+        }
+    }
+    if (SPG == 0) {
+        // one group: its scale products from the last stage's buffer (the
+        // scales are the same in every stage)
+        scale_products((stages - 1) & 1);
+        rescale(0);
+    } else if (!EARLY) {
+        // the last stage ends the last group
+        rescale(a.G - 1);
+    }
+
+    // --- epilogue: (mixed: x s_w[n]) -> fp16 (RNE) and optional fp32 ---
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = n0 + wn * 64 + nt * 32 + (lane & 31);
+            float swn = 1.0f;
+            if (MIXED && n < a.N) swn = a.sw[n];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
+                if (m < a.M && n < a.N) {
+                    float v = MIXED ? acc[mt][nt][r] * swn : acc[mt][nt][r];
+                    // keep the fp32 value: the multiply and the fp16 conversion
+                    // must not fuse into one rounding (y16 is the fp16 of y32)
+                    asm volatile("" : "+v"(v));
+                    const int64_t o = (int64_t)m * a.N + n;
+                    a.y16[o] = (_Float16)v;
+                    if (a.y32) a.y32[o] = v;
+                }
+            }
+        }
+}
+
+template <bool MIXED, bool DEBUG_P, int SPG>
+__global__ __launch_bounds__(THREADS, 2) void gemm_pp_kernel(PPArgs a)
+{
+    __shared__ PPShared sh;
+    // wave-uniform role (a scalar branch)
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x) < THREADS / 2)
+        pp_body<MIXED, DEBUG_P, SPG, true>(a, sh);
+    else
+        pp_body<MIXED, DEBUG_P, SPG, false>(a, sh);
+}
+
+template <bool MIXED, int SPG>
+void launch_pp(const PPArgs& t, hipStream_t stream)
+{
+    const dim3 grid((t.N + BN - 1) / BN, (t.M + BM - 1) / BM);
+    if (t.psum) gemm_pp_kernel<MIXED, true, SPG><<<grid, THREADS, 0, stream>>>(t);
+    else gemm_pp_kernel<MIXED, false, SPG><<<grid, THREADS, 0, stream>>>(t);
+}
+
+}  // namespace
+
+bool pingpong_supports(const GemmProblem& p)
+{
+    const int gs = p.ga < p.gw ? p.ga : p.gw;
+    const bool mixed = p.gw == p.K && p.ga != p.gw;
+    // groups of one stage (128) or one group (K).  (With groups of two
+    // stages, P and the scale products are live across more of the loop and
+    // the registers spill: the step-major tiled kernel is faster there.)
+    if (!(gs == KSTAGE || (gs == p.K && gs % KSTAGE == 0))) return false;
+    if (!mixed && p.ga != p.gw) return false;
+    // 32-bit buffer offsets within one workgroup's rows
+    const uint64_t rowbytes = (uint64_t)p.K / 2;
+    return rowbytes * BM < (1ull << 31) && (uint64_t)p.K / gs * 4 * BM < (1ull << 31);
+}
+
+hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
+{
+    PPArgs t;
+    t.qa = p.qa;
+    t.sa = p.sa;
+    t.qw = p.qw;
+    t.sw = p.sw;
+    t.M = p.M;
+    t.N = p.N;
+    t.K = p.K;
+    t.Ga = p.K / p.ga;
+    t.Gw = p.K / p.gw;
+    const int gs = p.ga < p.gw ? p.ga : p.gw;
+    t.spg = gs / KSTAGE;
+    t.G = p.K / gs;
+    t.y16 = static_cast<_Float16*>(p.y16);
+    t.y32 = p.y32;
+    t.psum = p.psum;
+    const bool mixed = p.gw == p.K && p.ga != p.gw;
+    // mixed mode here: ga = 128 (the activation groups are the stages)
+    if (mixed) launch_pp<true, 1>(t, stream);
+    else if (t.spg == 1) launch_pp<false, 1>(t, stream);
+    else launch_pp<false, 0>(t, stream);
+    return hipGetLastError();
+}
+
+}  // namespace apex4

@@ -24,10 +24,13 @@ struct GemmProblem {
 };
 
 // Picks the kernel for the shape: the skinny kernel (streams the weights; few
-// rows, groups >= 128) or the tiled kernel (everything else).
+// rows, groups >= 128), the ping-pong tiled kernel (groups of 128 or more) or
+// the tiled kernel (everything else).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
 hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
+bool pingpong_supports(const GemmProblem& p);
+hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
 bool skinny_supports(const GemmProblem& p);
 hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream);
 
