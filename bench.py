@@ -16,8 +16,11 @@ prefill, the granularity sweep) are selectable for measurement runs.
 
 Prints ONE JSON line: value = effective TOPS (sum of 2*M*N*K over the step's
 GEMMs / step time), plus a roofline object for the GEMM kernel (int8 MFMA
-peak, or HBM for memory-bound workloads) from HIP events around every GEMM
-launch of the timed region, and the CPU oracle timed on a bounded row sample.
+peak, or HBM for memory-bound workloads) and the CPU oracle timed on a
+bounded row sample.  The timed steps launch eagerly (--graph: replay one
+captured HIP graph per step).  The roofline's kernel duration comes from HIP
+events around back-to-back GEMM launches of each layer on the launch stream,
+so no host gap is counted in it.
 """
 from __future__ import annotations
 
@@ -68,6 +71,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per step instead of eager launches "
+                         "(eager launches keep the GPU busy here: the host enqueues faster than "
+                         "the kernels run, and a graph launch costs more than it saves)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="oracle rows per layer for the CPU baseline (0 = sized for ~12 s)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -76,7 +83,7 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
                          "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-decode-m16",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m16",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
@@ -99,38 +106,43 @@ def calibrate_copy():
 def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
     """Time the CPU oracle (quantize + GEMM) on the first rows of every layer.
 
-    rows_per_layer = 0 sizes the sample from a 4-row trial so the timed work
-    takes about target_s seconds.
+    rows_per_layer = 0 sizes the sample so that the timed work takes about
+    target_s seconds: a first pass on 16 rows per layer, then at most two
+    larger passes scaled from the last one; the last pass is reported.
     """
     from oracle import oracle
 
     o = oracle.default()
-    if rows_per_layer <= 0:
-        trial = 4
-        t = 0.0
+
+    def one_pass(rows):
+        ops, secs = 0.0, 0.0
         for (K, N) in layers:
-            x, w = inputs.problem(trial, N, K, seed=0, act=act)
-            qw, sw = o.quantize(w, gw)
+            x, w = inputs.problem(rows, N, K, seed=0, act=act)
+            qw, sw = o.quantize(w, gw)                   # offline on both sides: untimed
             t0 = time.perf_counter()
             qa, sa = o.quantize(x, ga)
             o.gemm(qa, sa, ga, qw, sw, gw, K, want_y32=False)
-            t += time.perf_counter() - t0
-        rows_per_layer = int(max(trial, min(M, trial * target_s / max(t, 1e-6))))
-    total_ops, total_s = 0.0, 0.0
-    for (K, N) in layers:
-        x, w = inputs.problem(rows_per_layer, N, K, seed=0, act=act)
-        qw, sw = o.quantize(w, gw)                       # offline on both sides: untimed
-        t0 = time.perf_counter()
-        qa, sa = o.quantize(x, ga)
-        o.gemm(qa, sa, ga, qw, sw, gw, K, want_y32=False)
-        total_s += time.perf_counter() - t0
-        total_ops += rl.gemm_ops(rows_per_layer, N, K)
+            secs += time.perf_counter() - t0
+            ops += rl.gemm_ops(rows, N, K)
+        return ops, secs
+
+    if rows_per_layer > 0:
+        rows = min(M, rows_per_layer)
+        total_ops, total_s = one_pass(rows)
+    else:
+        rows = min(M, 16)
+        total_ops, total_s = one_pass(rows)
+        for _ in range(2):
+            if total_s >= 0.5 * target_s or rows >= M:
+                break
+            rows = int(min(M, max(rows + 1, np.ceil(rows * target_s / max(total_s, 1e-6)))))
+            total_ops, total_s = one_pass(rows)
     return {
         "value": total_ops / total_s / 1e12,
         "unit": "TOPS",
         "cores": o.num_threads(),
         "kind": "oracle",
-        "sample": f"first {rows_per_layer} of {M} rows of every layer (quantize + GEMM, weights "
+        "sample": f"first {rows} of {M} rows of every layer (quantize + GEMM, weights "
                   f"pre-packed), {total_s:.1f} s",
     }
 
@@ -263,33 +275,75 @@ def main():
     ops_step = sum(rl.gemm_ops(M, N, K) for (K, N) in layers)
     bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) for (K, N) in layers]
 
-    def step(i, events=None):
-        for li, (K, N, tx, qa, sa, qw, sw, y) in enumerate(sets[i % copies]):
+    def step(i):
+        for (K, N, tx, qa, sa, qw, sw, y) in sets[i % copies]:
             apex4.quantize_act(tx, ga, out=(qa, sa))
-            if events is not None:
-                events[li][0].record()
             apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
-            if events is not None:
-                events[li][1].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, synchronized on both sides; GEMM launches bracketed by events
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in layers] for _ in range(args.steps)]
+    # --graph: one step per weight-copy set captured as a HIP graph and
+    # replayed in the timed region (default: eager launches)
+    graphs = None
+    if args.graph:
+        cap = torch.cuda.Stream()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is None:
+            step(i)
+        else:
+            graphs[i % copies].replay()
+
+    # timed region: K steps, synchronized on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(s, ev[s])
+        run(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
 
-    gemm_ms = np.array([[ev[s][li][0].elapsed_time(ev[s][li][1]) for li in range(len(layers))]
-                        for s in range(args.steps)])           # [steps, layers]
-    gemm_ms_avg = gemm_ms.mean(axis=0)
+    # GEMM kernel duration per layer, for the roofline: R back-to-back
+    # launches (cycling the weight copies) between two HIP events on the
+    # launch stream (one captured graph with --graph); the host enqueues
+    # ahead of the GPU, so no host gap sits inside the measured interval
+    R = max(copies, 8)
+    gemm_ms_avg = []
+    launch = torch.cuda.current_stream()
+    for li, (K, N) in enumerate(layers):
+        def gemms():
+            for r in range(R):
+                (_, _, _, qa, sa, qw, sw, y) = sets[r % copies][li]
+                apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
+        if graphs is not None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                gemms()
+            body = g.replay
+        else:
+            body = gemms
+        body()
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(launch)
+        for _ in range(reps):
+            body()
+        e1.record(launch)
+        torch.cuda.synchronize()
+        gemm_ms_avg.append(e0.elapsed_time(e1) / (reps * R))
+    gemm_ms_avg = np.array(gemm_ms_avg)
     layer_ops = np.array([rl.gemm_ops(M, N, K) for (K, N) in layers])
     if bound == "mfma":
         achieved = float(layer_ops.sum() / (gemm_ms_avg.sum() * 1e-3)) / 1e12
@@ -325,12 +379,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "layers_KN": layers, "group_a": ga, "group_w": gw,
                    "activations": act, "timed": "quantize_act + gemm per layer",
+                   "launch": "eager" if graphs is None else "HIP graph per step",
                    "weight_copies_cycled": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
-                     "kernel": "gemm (apex4_gemm_w4a4)"},
+                     "kernel": "gemm (apex4_gemm_w4a4)",
+                     "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
