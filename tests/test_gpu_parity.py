@@ -163,6 +163,21 @@ def test_gemm_ragged_shapes(dev, M, N, K, g):
     run_case(dev, x, w, g, g, want_p=True)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("ga,gw", [(128, 128), (256, 256), ("K", "K"), (128, "K")])
+@pytest.mark.parametrize("K", [2048, 9216])
+def test_gemm_decode_rows(dev, M, ga, gw, K):
+    """Up to 4 rows: the row-streaming kernel (whole weight rows per wave, dot8
+    products); 5 and 8 rows: the skinny MFMA kernel.  K = 2048 leaves most
+    lanes without a unit; K = 9216 (72 units) gives lanes a second, partial
+    pass; N = 300 is not a multiple of the wave count; group sums P are
+    compared too."""
+    ga = K if ga == "K" else ga
+    gw = K if gw == "K" else gw
+    x, w = inputs.problem(M, 300, K, seed=11 + M, act="outlier")
+    run_case(dev, x, w, ga, gw, want_p=True)
+
+
 @pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
 def test_gemm_unit_scales_integer_exact(dev, g):
     """Random packed codes (-8 included), all scales 1: Y is the exact integer matmul."""

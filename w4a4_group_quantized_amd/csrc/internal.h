@@ -23,14 +23,17 @@ struct GemmProblem {
     int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
 };
 
-// Picks the kernel for the shape: the skinny kernel (streams the weights; few
-// rows, groups >= 128), the ping-pong tiled kernel (groups of 128 or more) or
-// the tiled kernel (everything else).
+// Picks the kernel for the shape: the row-streaming dot8 kernel (M <= 4), the
+// skinny MFMA kernel (M <= 64; both stream the weights, groups >= 128), the
+// ping-pong tiled kernel (groups of 128 or one group over K) or the tiled
+// kernel (everything else).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
 hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
 bool pingpong_supports(const GemmProblem& p);
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
+bool gemv_supports(const GemmProblem& p);
+hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);
 bool skinny_supports(const GemmProblem& p);
 hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream);
 
