@@ -11,6 +11,9 @@ namespace apex4 {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
 {
     if (gemv_supports(p)) return launch_gemm_gemv(p, stream);
+#ifndef APEX4_NO_STREAM
+    if (stream_supports(p)) return launch_gemm_stream(p, stream);
+#endif
     if (skinny_supports(p)) return launch_gemm_skinny(p, stream);
 #ifndef APEX4_NO_PINGPONG
     if (pingpong_supports(p)) return launch_gemm_pingpong(p, stream);

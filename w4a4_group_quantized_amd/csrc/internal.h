@@ -24,9 +24,9 @@ struct GemmProblem {
 };
 
 // Picks the kernel for the shape: the row-streaming dot8 kernel (M <= 4), the
-// skinny MFMA kernel (M <= 64; both stream the weights, groups >= 128), the
-// ping-pong tiled kernel (groups of 128 or one group over K) or the tiled
-// kernel (everything else).
+// LDS-streaming MFMA kernel (M <= 16), the skinny MFMA kernel (M <= 64; these
+// three stream the weights, groups >= 128), the ping-pong tiled kernel
+// (groups of 128 or one group over K) or the tiled kernel (everything else).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
 hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
@@ -34,6 +34,8 @@ bool pingpong_supports(const GemmProblem& p);
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
 bool gemv_supports(const GemmProblem& p);
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);
+bool stream_supports(const GemmProblem& p);
+hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);
 bool skinny_supports(const GemmProblem& p);
 hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream);
 
