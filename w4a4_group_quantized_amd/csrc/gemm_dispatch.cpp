@@ -1,19 +1,21 @@
 // Kernel choice for apex4_gemm_w4a4.  Few rows: the call is bound by reading
-// the packed weights once; up to 4 rows the dot8 kernel streams whole weight
-// rows per wave, up to 64 the skinny kernel feeds the matrix units.
-// Otherwise the call is compute-bound and one of the tiled kernels runs (the
-// ping-pong one for groups of 128 or one group over K, the step-major one for
-// the other group sizes).
+// the packed weights once; up to 2 rows the dot8 kernel streams whole weight
+// rows per wave, up to 16 the LDS-streaming MFMA kernel, up to 64 the skinny
+// kernel feeds the matrix units from global memory.  Otherwise the call is
+// compute-bound and one of the tiled kernels runs (the ping-pong one for
+// groups of 128 or one group over K, the step-major one for the other group
+// sizes).
 #include "internal.h"
 
 namespace apex4 {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
 {
-    if (gemv_supports(p)) return launch_gemm_gemv(p, stream);
+    if (p.M <= 2 && gemv_supports(p)) return launch_gemm_gemv(p, stream);
 #ifndef APEX4_NO_STREAM
     if (stream_supports(p)) return launch_gemm_stream(p, stream);
 #endif
+    if (gemv_supports(p)) return launch_gemm_gemv(p, stream);
     if (skinny_supports(p)) return launch_gemm_skinny(p, stream);
 #ifndef APEX4_NO_PINGPONG
     if (pingpong_supports(p)) return launch_gemm_pingpong(p, stream);

@@ -64,17 +64,30 @@ struct StreamArgs {
     int32_t* psum;
 };
 
-// One item in LDS: 16 weight-row pieces, 16 activation-row pieces, and the
-// scales of the item's groups: s_w as [16 rows][16 groups], then s_a as
-// [16 groups][16 rows] (groups past the item's, rows past M: zeros).  One
-// group over K (or per-channel weight scales): group 0 only.
-struct ItemBuf {
-    uint8_t q[2 * ROWS * PIECE];
-    float sc[2 * ROWS * 16];
+// One item in LDS: 16 weight-row pieces, ACT activation-row pieces (ACT = 4,
+// 8 or 16 >= M; the fragments of rows i >= ACT read row i mod ACT, whose
+// outputs are never stored), and the scales of the item's groups: s_w as
+// [16 rows][16 groups], then s_a as [16 groups][16 rows] (groups past the
+// item's, rows past M: zeros; one group over K or per-channel weight scales:
+// group 0 only).  RES: the ACT activation rows are instead copied to LDS
+// once, whole ([row][item] pieces after the buffers), when they fit; every
+// load an item needs beyond its weights costs streaming rate.  Without RES,
+// the fewer activation rows an item holds, the more buffers fit.
+constexpr int SC_BYTES = 2 * ROWS * 16 * 4;
+template <int ACT, bool RES>
+struct Item {
+    static constexpr int A = ROWS * PIECE;                     // activation pieces (not RES)
+    static constexpr int SC = RES ? A : A + ACT * PIECE;       // scales
+    static constexpr int BYTES = SC + SC_BYTES;
+    static constexpr int NBUF = RES || ACT == 16 ? 4 : ACT == 8 ? 5 : 6;  // buffers
+    static constexpr int RES_A = NBUF * BYTES;                 // resident activation rows (RES)
+    static constexpr int VM = RES ? 3 : 2 + (ACT == 16 ? 2 : 1) + 1;  // vector memory operations per wave and item
 };
-constexpr int NBUF = 4;                  // item buffers; copies run NBUF - 1 items ahead
-constexpr int VM_ITEM = 5;               // vector memory operations per wave and item
-__shared__ ItemBuf lds_i0, lds_i1, lds_i2, lds_i3;
+constexpr int ITEM_LDS = 144 * 1024;
+static_assert(Item<16, false>::RES_A <= ITEM_LDS && Item<8, false>::RES_A <= ITEM_LDS &&
+                  Item<4, false>::RES_A <= ITEM_LDS, "item buffers");
+constexpr int RES_MAX = ITEM_LDS - Item<16, true>::RES_A;     // bytes of resident activation rows
+__shared__ __attribute__((aligned(16))) uint8_t lds_items[ITEM_LDS];
 // the waves' partial tiles of a block, two blocks apart (a block of a single
 // item is finished after the next barrier while the next block is written)
 __shared__ __attribute__((aligned(16))) float lds_red[2][WAVES * 64 * 4];
@@ -188,16 +201,14 @@ __device__ inline v4i widen_hi(uint4 w)
 
 constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-__device__ inline ItemBuf& item_buf(int i)
-{
-    return i == 0 ? lds_i0 : i == 1 ? lds_i1 : i == 2 ? lds_i2 : lds_i3;
-}
-
 // GM: 1 (groups of 128), 2 (groups of 256), 0 (one group over K).  MIXED:
-// per-channel weight scales, activation groups of 128.
-template <int GM, bool MIXED, bool DEBUG_P>
+// per-channel weight scales, activation groups of 128.  ACT: activation rows
+// held (M <= ACT); RES: held whole, not per item.
+template <int GM, bool MIXED, bool DEBUG_P, int ACT, bool RES>
 __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
 {
+    using L = Item<ACT, RES>;
+    constexpr int NBUF = L::NBUF;
     constexpr bool SW_PER_GROUP = GM != 0 && !MIXED;       // s_w varies along K
     constexpr bool SA_PER_GROUP = GM != 0;                 // s_a varies along K
     constexpr int GPI = GM == 2 ? IK / 256 : IK / 128;     // groups per item (GM 1, 2)
@@ -211,42 +222,57 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
     const __amdgpu_buffer_rsrc_t rS = buffer_of(a.sw, (uint32_t)a.N * a.Gw * 4);
     const __amdgpu_buffer_rsrc_t rSA = buffer_of(a.sa, (uint32_t)a.M * a.Ga * 4);
 
-    // --- copy of item t: this wave fills weight rows 2w, 2w+1 and activation
-    // rows 2w, 2w+1 (lane l fetches chunk l ^ r of row r), and one quarter
-    // of the scales: waves 0-3 s_w of rows 4w..4w+3, waves 4-7 s_a of the
-    // item's groups 4(w-4)..4(w-4)+3; lane l brings one value ---
-    auto copy_item = [&](ItemBuf& d, int t) {
+    // --- copy of item t into buffer bi: this wave fills weight rows 2w, 2w+1
+    // and activation rows 2w, 2w+1 (ACT = 16) or w mod ACT (lane l fetches
+    // chunk l ^ r of row r; a row that two waves fetch gets the same bytes
+    // twice), and one quarter of the scales: waves 0-3 s_w of rows
+    // 4w..4w+3, waves 4-7 s_a of the item's groups 4(w-4)..4(w-4)+3; lane l
+    // brings one value ---
+    auto copy_item = [&](int bi, int t) {
+        uint8_t* d = lds_items + bi * L::BYTES;
+        float* dsc = reinterpret_cast<float*>(d + L::SC);
         const int b = blockIdx.x + gridDim.x * (t / a.items), it = t % a.items;
         const bool live = t < total;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 2 * wave + (j & 1);
+        for (int j = 0; j < (RES ? 2 : ACT == 16 ? 4 : 3); ++j) {
             const bool act = j >= 2;
+            const int r = act && ACT < 16 ? wave % ACT : 2 * wave + (j & 1);
             const uint32_t pos = (uint32_t)it * PIECE + 16 * (lane ^ r);   // byte within the row
             const uint32_t row = act ? (uint32_t)r : (uint32_t)(b * ROWS + r);
-            const bool in = live && pos < rowbytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(act ? rA : rW, (lds_void*)(d.q + (act ? ROWS : 0) * PIECE + r * PIECE),
-                                                     16, in ? (int)(row * rowbytes + pos) : (int)OOB, 0, 0, 0);
+            const bool in = live && pos < rowbytes && (!act || r < a.M);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(act ? rA : rW, (lds_void*)(d + (act ? L::A : 0) + r * PIECE), 16,
+                                                     in ? (int)(row * rowbytes + pos) : (int)OOB, 0, 0, 0);
         }
         if (wave < 4) {
             const int n = b * ROWS + 4 * wave + (lane >> 4), gi = lane & 15;
             const int g = SW_PER_GROUP ? it * GPI + gi : 0;
             const bool in = live && n < a.N && (SW_PER_GROUP ? gi < GPI && g < a.Gw : gi == 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(d.sc + 64 * wave), 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(dsc + 64 * wave), 4,
                                                      in ? (int)(((uint32_t)n * a.Gw + g) * 4) : (int)OOB, 0, 0, 0);
         } else {
             const int m = lane & 15, gi = 4 * (wave - 4) + (lane >> 4);
             const int g = SA_PER_GROUP ? it * GPI + gi : 0;
             const bool in = live && m < a.M && (SA_PER_GROUP ? gi < GPI && g < a.Ga : gi == 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void*)(d.sc + 64 * wave), 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void*)(dsc + 64 * wave), 4,
                                                      in ? (int)(((uint32_t)m * a.Ga + g) * 4) : (int)OOB, 0, 0, 0);
         }
     };
 
+    // RES: the activation rows, piece p = row * items + item (lane l fetches
+    // chunk l ^ row); these copies are older than every item's, so the
+    // first barrier's wait covers them
+    if (RES) {
+        for (int p = wave; p < ACT * a.items; p += WAVES) {
+            const int r = p / a.items, it = p - r * a.items;
+            const uint32_t pos = (uint32_t)it * PIECE + 16 * (lane ^ r);
+            const bool in = r < a.M && pos < rowbytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(lds_items + L::RES_A + p * PIECE), 16,
+                                                     in ? (int)(r * rowbytes + pos) : (int)OOB, 0, 0, 0);
+        }
+    }
     // the first NBUF - 1 items in flight
-    copy_item(lds_i0, 0);
-    copy_item(lds_i1, 1);
-    copy_item(lds_i2, 2);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) copy_item(i, i);
 
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4i P[2] = {v4i{}, v4i{}};
@@ -303,14 +329,15 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
     for (int h = 0; h < NBUF; ++h) {
         const int t = t0 + h;
         if (t >= total) break;
-        ItemBuf& cur = item_buf(h);
+        const uint8_t* cur = lds_items + h * L::BYTES;
+        const float* csc = reinterpret_cast<const float*>(cur + L::SC);
         const int hn = (h + NBUF - 1) % NBUF;              // (t + NBUF - 1) % NBUF, also t - 1's
         // item t has landed (the operations of the NBUF - 2 later items stay
         // in flight), and every wave is done with item t-1, whose buffer the
         // copy of t + NBUF - 1 reuses
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt(VM_ITEM * (NBUF - 2), 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt(L::VM * (NBUF - 2), 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -318,26 +345,29 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
             finish_block(prev_block, prev_k);
             prev_block = -1;
         }
-        copy_item(item_buf(hn), t + NBUF - 1);
+        copy_item(hn, t + NBUF - 1);
 
         const int b = blockIdx.x + gridDim.x * (t / a.items), it = t % a.items;
         // fragments: chunks 8w + kb and 8w + 4 + kb of row fi, swizzled
-        const uint8_t* wrow = cur.q + fi * PIECE;
-        const uint8_t* arow = cur.q + (ROWS + fi) * PIECE;
+        // (activations: of row fi mod ACT)
+        const int fa = fi & (ACT - 1);
+        const uint8_t* wrow = cur + fi * PIECE;
+        const uint8_t* arow = RES ? lds_items + L::RES_A + (fa * a.items + it) * PIECE : cur + L::A + fa * PIECE;
         const int c0 = (8 * wave + fkb) ^ fi, c1 = (8 * wave + 4 + fkb) ^ fi;
+        const int a0 = (8 * wave + fkb) ^ fa, a1 = (8 * wave + 4 + fkb) ^ fa;
         uint4 w0, w1, x0, x1;
         // this wave's groups of the item: 2w, 2w + 1 (groups of 128) or w
         const int gi0 = GM == 1 ? 2 * wave : wave;
         v4f sa4[2];
         float sw2[2];
         if (GM != 0)
-            lds_read_item(lds_addr(wrow + 16 * c0), lds_addr(wrow + 16 * c1), lds_addr(arow + 16 * c0),
-                          lds_addr(arow + 16 * c1), lds_addr(&cur.sc[256 + gi0 * 16 + m_out]),
-                          lds_addr(&cur.sc[256 + (gi0 + 1) * 16 + m_out]), lds_addr(&cur.sc[n_lane * 16 + gi0]),
-                          lds_addr(&cur.sc[n_lane * 16 + gi0 + 1]), w0, w1, x0, x1, sa4[0], sa4[1], sw2[0], sw2[1]);
+            lds_read_item(lds_addr(wrow + 16 * c0), lds_addr(wrow + 16 * c1), lds_addr(arow + 16 * a0),
+                          lds_addr(arow + 16 * a1), lds_addr(&csc[256 + gi0 * 16 + m_out]),
+                          lds_addr(&csc[256 + (gi0 + 1) * 16 + m_out]), lds_addr(&csc[n_lane * 16 + gi0]),
+                          lds_addr(&csc[n_lane * 16 + gi0 + 1]), w0, w1, x0, x1, sa4[0], sa4[1], sw2[0], sw2[1]);
         else
-            lds_read_frag(lds_addr(wrow + 16 * c0), lds_addr(wrow + 16 * c1), lds_addr(arow + 16 * c0),
-                          lds_addr(arow + 16 * c1), w0, w1, x0, x1);
+            lds_read_frag(lds_addr(wrow + 16 * c0), lds_addr(wrow + 16 * c1), lds_addr(arow + 16 * a0),
+                          lds_addr(arow + 16 * a1), w0, w1, x0, x1);
         if (GM == 1) {
             P[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_lo(x0), widen_lo(w0), v4i{}, 0, 0, 0);
             P[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_hi(x0), widen_hi(w0), P[0], 0, 0, 0);
@@ -393,7 +423,7 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
                 for (int r = 0; r < 4; ++r) acc[r] = 0.0f;
             }
             if ((GM == 0 || MIXED) && tid < ROWS * ROWS)
-                lds_read_2(lds_addr(&cur.sc[256 + f_m]), lds_addr(&cur.sc[f_nl * 16]), s_a0, s_w0);
+                lds_read_2(lds_addr(&csc[256 + f_m]), lds_addr(&csc[f_nl * 16]), s_a0, s_w0);
             prev_block = b;
             prev_k = k;
         }
@@ -403,13 +433,26 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
     if (prev_block >= 0) finish_block(prev_block, prev_k);
 }
 
+template <int GM, bool MIXED, int ACT>
+hipError_t launch_act(const StreamArgs& s, bool dbg, hipStream_t stream)
+{
+    const int grid = s.blocks < 256 ? s.blocks : 256;
+    if ((int64_t)ACT * s.items * PIECE <= RES_MAX) {
+        if (dbg) gemm_stream_kernel<GM, MIXED, true, ACT, true><<<grid, THREADS, 0, stream>>>(s);
+        else gemm_stream_kernel<GM, MIXED, false, ACT, true><<<grid, THREADS, 0, stream>>>(s);
+    } else {
+        if (dbg) gemm_stream_kernel<GM, MIXED, true, ACT, false><<<grid, THREADS, 0, stream>>>(s);
+        else gemm_stream_kernel<GM, MIXED, false, ACT, false><<<grid, THREADS, 0, stream>>>(s);
+    }
+    return hipGetLastError();
+}
+
 template <int GM, bool MIXED>
 hipError_t launch_gm(const StreamArgs& s, bool dbg, hipStream_t stream)
 {
-    const int grid = s.blocks < 256 ? s.blocks : 256;
-    if (dbg) gemm_stream_kernel<GM, MIXED, true><<<grid, THREADS, 0, stream>>>(s);
-    else gemm_stream_kernel<GM, MIXED, false><<<grid, THREADS, 0, stream>>>(s);
-    return hipGetLastError();
+    if (s.M <= 4) return launch_act<GM, MIXED, 4>(s, dbg, stream);
+    if (s.M <= 8) return launch_act<GM, MIXED, 8>(s, dbg, stream);
+    return launch_act<GM, MIXED, 16>(s, dbg, stream);
 }
 
 }  // namespace
