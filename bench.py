@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
                          "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m16",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
@@ -147,29 +147,50 @@ def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
     }
 
 
-def kernel_sources_sha256():
-    """sha256 over the library's kernel sources (every file name and content
-    under w4a4_group_quantized_amd/csrc, in name order)."""
+CSRC = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc")
+# sources every GEMM launch goes through (kernel choice, shared declarations)
+COMMON_SOURCES = ("gemm_dispatch.cpp", "internal.h")
+
+
+def kernel_sources_sha256(files):
+    """sha256 over the named kernel sources under w4a4_group_quantized_amd/csrc
+    (each file name and content, in name order)."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            h.update(name.encode() + b"\0")
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(files):
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
+
+
+def kernel_source_files(kernel_names):
+    """The csrc files that define the given kernels (profiler kernel names),
+    plus the common dispatch sources."""
+    import re
+    idents = set()
+    for k in kernel_names:
+        idents.update(re.findall(r"(\w+_kernel)\b", k))
+    files = set(COMMON_SOURCES)
+    for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".cpp")):
+            continue
+        with open(os.path.join(CSRC, name)) as f:
+            text = f.read()
+        if any(re.search(r"void\s+" + i + r"\s*\(", text) for i in idents):
+            files.add(name)
+    return sorted(files)
 
 
 def measured_traffic(workload):
     """Mean HBM bytes per GEMM launch from the committed rocprofv3 counters
     (profiles/hbm_traffic.json), or None when that workload was not counted
-    or the kernel sources changed since."""
+    or the sources of its kernels changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)["workloads"][workload]
-        if rec["kernel_sources_sha256"] != kernel_sources_sha256():
+        if rec["kernel_sources_sha256"] != kernel_sources_sha256(rec["kernel_sources"]):
             return None
         return rec["hbm_bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -204,12 +225,13 @@ def write_traffic(prof_dir, workloads):
     out = {"description": "HBM bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                           "(KiB per dispatch), each scaled by the factor that makes the same counter read "
                           "1 GiB for a plain 1 GiB device copy; written by python bench.py --write-traffic. "
-                          "bench.py reports them only while the kernel sources hash the same.",
+                          "bench.py reports them only while the sources of the workload's kernels hash the same.",
            "calibration": cal, "workloads": {}}
-    sha = kernel_sources_sha256()
     for wl in workloads:
         _, M, layers, ga, gw, _ = WORKLOADS[wl]
         gemm = lambda c: [v for _, k, v in rows(c, wl) if "gemm" in k and "quantize" not in k]
+        names = {k for _, k, _ in rows("FETCH_SIZE", wl) if "gemm" in k and "quantize" not in k}
+        files = kernel_source_files(names)
         fr, wr = gemm("FETCH_SIZE"), gemm("WRITE_SIZE")
         per = []
         for li, (K, N) in enumerate(layers):
@@ -220,7 +242,8 @@ def write_traffic(prof_dir, workloads):
                         "write_bytes": sum(w) / len(w) * 1024 * cal["write_factor"],
                         "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw)})
         out["workloads"][wl] = {
-            "kernel_sources_sha256": sha,
+            "kernel_sources": files,
+            "kernel_sources_sha256": kernel_sources_sha256(files),
             "hbm_bytes_per_launch": float(np.mean([p["fetch_bytes"] + p["write_bytes"] for p in per])),
             "algorithmic_bytes_per_launch": float(np.mean([p["algorithmic_bytes"] for p in per])),
             "per_layer": per,
