@@ -163,18 +163,35 @@ def test_gemm_ragged_shapes(dev, M, N, K, g):
     run_case(dev, x, w, g, g, want_p=True)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 17, 32, 33, 64])
 @pytest.mark.parametrize("ga,gw", [(128, 128), (256, 256), ("K", "K"), (128, "K")])
 @pytest.mark.parametrize("K", [2048, 9216])
 def test_gemm_decode_rows(dev, M, ga, gw, K):
-    """Up to 4 rows: the row-streaming kernel (whole weight rows per wave, dot8
-    products); 5 and 8 rows: the skinny MFMA kernel.  K = 2048 leaves most
-    lanes without a unit; K = 9216 (72 units) gives lanes a second, partial
-    pass; N = 300 is not a multiple of the wave count; group sums P are
-    compared too."""
+    """The decode kernels: 1-2 rows the row-streaming dot8 kernel (K = 2048
+    leaves most lanes without a unit, K = 9216 = 72 units gives lanes a second,
+    partial pass); 3-16 rows the LDS-streaming MFMA kernel (4, 8 or 16
+    activation rows held; K = 9216 ends in half an item); 17-64 rows its
+    K-outer variant (2 or 4 row tiles).  N = 300 is not a multiple of 16 or of
+    the wave count; group sums P are compared too."""
     ga = K if ga == "K" else ga
     gw = K if gw == "K" else gw
     x, w = inputs.problem(M, 300, K, seed=11 + M, act="outlier")
+    run_case(dev, x, w, ga, gw, want_p=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 9000, 4224), (64, 9000, 4224), (48, 5000, 2048), (12, 9000, 20480),
+                                   (4, 9000, 36864), (4, 3000, 40960)])
+@pytest.mark.parametrize("ga,gw", [(128, 128), (128, "K")])
+def test_gemm_decode_many_blocks(dev, M, N, K, ga, gw):
+    """Decode shapes with several 16-column blocks per workgroup: the K-outer
+    kernel with groups of 4 blocks (24 rows, 563 blocks) and of 2 (64 and 48
+    rows, the last group half empty at 9000 columns), K = 4224 ending in a
+    128-value item; the LDS-streaming kernel with the activation rows brought
+    per item because they do not fit whole (12 rows of K = 20480, 4 rows of
+    K = 40960), and held whole when they just fit (4 rows of K = 36864)."""
+    ga = K if ga == "K" else ga
+    gw = K if gw == "K" else gw
+    x, w = inputs.problem(M, N, K, seed=31 + M, act="outlier")
     run_case(dev, x, w, ga, gw, want_p=True)
 
 

@@ -1,7 +1,8 @@
 // Kernel choice for apex4_gemm_w4a4.  Few rows: the call is bound by reading
 // the packed weights once; up to 2 rows the dot8 kernel streams whole weight
-// rows per wave, up to 16 the LDS-streaming MFMA kernel, up to 64 the skinny
-// kernel feeds the matrix units from global memory.  Otherwise the call is
+// rows per wave, up to 16 the LDS-streaming MFMA kernel, up to 64 its variant
+// with K outside the column blocks (the skinny kernel, feeding the matrix
+// units from global memory, covers the group modes those lack).  Otherwise the call is
 // compute-bound and one of the tiled kernels runs (the ping-pong one for
 // groups of 128 or one group over K, the step-major one for the other group
 // sizes).
@@ -16,6 +17,9 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
     if (stream_supports(p)) return launch_gemm_stream(p, stream);
 #endif
     if (gemv_supports(p)) return launch_gemm_gemv(p, stream);
+#ifndef APEX4_NO_KOUTER
+    if (kouter_supports(p)) return launch_gemm_kouter(p, stream);
+#endif
     if (skinny_supports(p)) return launch_gemm_skinny(p, stream);
 #ifndef APEX4_NO_PINGPONG
     if (pingpong_supports(p)) return launch_gemm_pingpong(p, stream);

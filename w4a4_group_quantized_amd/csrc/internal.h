@@ -23,9 +23,10 @@ struct GemmProblem {
     int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
 };
 
-// Picks the kernel for the shape: the row-streaming dot8 kernel (M <= 4), the
-// LDS-streaming MFMA kernel (M <= 16), the skinny MFMA kernel (M <= 64; these
-// three stream the weights, groups >= 128), the ping-pong tiled kernel
+// Picks the kernel for the shape: the row-streaming dot8 kernel (M <= 2), the
+// LDS-streaming MFMA kernels (M <= 16, and 17..64 with K outside the column
+// blocks), the skinny MFMA kernel (M <= 64, the group modes those two lack;
+// these four stream the weights, groups >= 128), the ping-pong tiled kernel
 // (groups of 128 or one group over K) or the tiled kernel (everything else).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
@@ -36,6 +37,8 @@ bool gemv_supports(const GemmProblem& p);
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);
 bool stream_supports(const GemmProblem& p);
 hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);
+bool kouter_supports(const GemmProblem& p);
+hipError_t launch_gemm_kouter(const GemmProblem& p, hipStream_t stream);
 bool skinny_supports(const GemmProblem& p);
 hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream);
 
