@@ -179,6 +179,18 @@ def test_gemm_decode_rows(dev, M, ga, gw, K):
     run_case(dev, x, w, ga, gw, want_p=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 300, 1024), (260, 130, 2560), (513, 257, 3328)])
+@pytest.mark.parametrize("ga,gw", [(256, 256), (256, "K")])
+def test_gemm_groups_of_two_stages(dev, M, N, K, ga, gw):
+    """Groups of 256 (and mixed mode with activation groups of 256) on the
+    ping-pong tiled kernel: a group spans two 128-value stages, so the int32
+    sums run across a stage boundary before the rescale; 10 and 13 groups
+    (odd), ragged M and N."""
+    gw = K if gw == "K" else gw
+    x, w = inputs.problem(M, N, K, seed=41 + M, act="outlier")
+    run_case(dev, x, w, ga, gw, want_p=True)
+
+
 @pytest.mark.parametrize("M,N,K", [(24, 9000, 4224), (64, 9000, 4224), (48, 5000, 2048), (12, 9000, 20480),
                                    (4, 9000, 36864), (4, 3000, 40960)])
 @pytest.mark.parametrize("ga,gw", [(128, 128), (128, "K")])

@@ -146,8 +146,8 @@ __device__ inline void lds_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// SPG: stages per group, 1 (g = 128) or 0 (one group, g = K).  EARLY: this
-// wave belongs to waves 0..3.
+// SPG: stages per group, 1 (g = 128), 2 (g = 256) or 0 (one group, g = K).
+// EARLY: this wave belongs to waves 0..3.
 template <bool MIXED, bool DEBUG_P, int SPG, bool EARLY>
 __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
 {
@@ -196,7 +196,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             rq[set][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
         // the scale of the group that stage t belongs to
-        const int g = (SPG == 1 ? t : 0) * 4;
+        const int g = (SPG == 1 ? t : SPG == 2 ? t >> 1 : 0) * 4;
         if (EARLY || !MIXED)
             rs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g, 0));
     };
@@ -288,25 +288,36 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         const uint8_t* la = sh.a[buf] + frag;
         const uint8_t* lb = sh.b[buf] + fragb;
         v4i fa[2][4], fb[2][4];
+        if (zero) {
+            // P starts here: all fragments first
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
-                fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
+                for (int i = 0; i < 2; ++i) {
+                    fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
+                    fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
+                }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (!zero) {
+                // P is live from the stage before (groups of two stages): the
+                // fragments K-step by K-step (kept apart by scheduling
+                // barriers), fewer registers at once
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
+                    fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
+                }
             }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][0], fb[nt][0], zero ? v16i{} : P[mt][nt], 0, 0, 0);
-#pragma unroll
-        for (int s = 1; s < 4; ++s)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][s], fb[nt][s], P[mt][nt], 0, 0, 0);
+                    P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][s], fb[nt][s],
+                                                                      (zero && s == 0) ? v16i{} : P[mt][nt], 0, 0, 0);
+        }
         if (ends) scale_products(buf);
     };
 
@@ -370,8 +381,11 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     for (int h = 0; h < 2; ++h) {
         const int t = t0 + h;
         if (t >= stages) break;
-        constexpr bool zero = SPG == 1;   // stage t starts a group
-        constexpr bool ends = SPG == 1;   // stage t ends a group
+        // (t and h have the same parity)
+        const bool zero = SPG == 1 || (SPG == 2 && h == 0);   // stage t starts a group
+        const bool ends = SPG == 1 || (SPG == 2 && h == 1);   // stage t ends a group
+        const bool prev_ends = SPG == 1 || (SPG == 2 && h == 0);   // stage t-1 ended one
+        const int grp = SPG == 2 ? t >> 1 : t;                // the group of stage t
         // The copy runs in every stage, also past the last one: loads past the
         // end of K read other rows or zeros, and the stores go to a buffer
         // that is no longer read; unconditional memory operations keep the
@@ -379,20 +393,34 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         if (EARLY) {
             // phase 1: matrix work of stage t, copy of stage t+1
             load_stage(t + 2, h);
-            mma_stage(h, zero, ends);
-            store_stage(h ^ 1, h ^ 1);
+            if (SPG == 2) {
+                // groups of two stages: the stored registers freed before the
+                // MFMAs (P stays live across stages here)
+                store_stage(h ^ 1, h ^ 1);
+                mma_stage(h, zero, ends);
+            } else {
+                mma_stage(h, zero, ends);
+                store_stage(h ^ 1, h ^ 1);
+            }
             lds_barrier();
-            // phase 2: rescale of stage t
-            if (ends) rescale(t);
+            // phase 2: rescale of stage t's group when the stage ends it
+            if (ends) rescale(grp);
             lds_barrier();
         } else {
-            // phase 1: rescale of stage t-1
-            if (ends && t > 0) rescale(t - 1);
+            // phase 1: rescale of stage t-1's group when that stage ended it
+            if (prev_ends && t > 0) rescale(SPG == 2 ? (t - 1) >> 1 : t - 1);
             lds_barrier();
             // phase 2: matrix work of stage t, copy of stage t+1
             load_stage(t + 2, h);
-            mma_stage(h, zero, ends);
-            store_stage(h ^ 1, h ^ 1);
+            if (SPG == 2) {
+                // groups of two stages: the stored registers freed before the
+                // MFMAs (P stays live across stages here)
+                store_stage(h ^ 1, h ^ 1);
+                mma_stage(h, zero, ends);
+            } else {
+                mma_stage(h, zero, ends);
+                store_stage(h ^ 1, h ^ 1);
+            }
             lds_barrier();
         }
     }
@@ -455,11 +483,11 @@ bool pingpong_supports(const GemmProblem& p)
 {
     const int gs = p.ga < p.gw ? p.ga : p.gw;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
-    // groups of one stage (128) or one group (K).  (With groups of two
-    // stages, P and the scale products are live across more of the loop and
-    // the registers spill: the step-major tiled kernel is faster there.)
-    if (!(gs == KSTAGE || (gs == p.K && gs % KSTAGE == 0))) return false;
+    // groups of one stage (128), two stages (256) or one group (K); mixed
+    // mode with activation groups of one or two stages
+    if (!(gs == KSTAGE || gs == 2 * KSTAGE || (gs == p.K && gs % KSTAGE == 0))) return false;
     if (!mixed && p.ga != p.gw) return false;
+    if (mixed && p.ga != KSTAGE && p.ga != 2 * KSTAGE) return false;
     // 32-bit buffer offsets within one workgroup's rows
     const uint64_t rowbytes = (uint64_t)p.K / 2;
     return rowbytes * BM < (1ull << 31) && (uint64_t)p.K / gs * 4 * BM < (1ull << 31);
@@ -484,10 +512,12 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.y32 = p.y32;
     t.psum = p.psum;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
-    // mixed mode here: ga = 128 (the activation groups are the stages)
-    if (mixed) launch_pp<true, 1>(t, stream);
+    // mixed mode here: ga = 128 or 256 (the activation groups are 1 or 2 stages)
+    if (mixed && t.spg == 1) launch_pp<true, 1>(t, stream);
+    else if (mixed) launch_pp<true, 2>(t, stream);
     else if (t.spg == 1) launch_pp<false, 1>(t, stream);
-    else launch_pp<false, 0>(t, stream);
+    else if (gs == p.K) launch_pp<false, 0>(t, stream);
+    else launch_pp<false, 2>(t, stream);
     return hipGetLastError();
 }
 
