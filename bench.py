@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
                          "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
