@@ -126,12 +126,14 @@ __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane
 struct PPShared {
     uint8_t a[2][A_BYTES];
     uint8_t b[2][B_BYTES];
-    // Scale operands, per stage buffer: one 32-byte row per tile row, the bf16
-    // pieces in slots 0..5 and zeros in slots 6..15 (lanes 32..63 of the
-    // split-operand MFMA read the upper, zero half), or in mixed mode fp32
-    // 2^-8 s_a in the first BM dwords of ta.
-    uint4 ta[2][BM][2];
-    uint4 tb[2][BN][2];
+    // Scale operands, per stage buffer: two 16-byte halves per tile row, half
+    // 0 holding the bf16 pieces in slots 0..5 and zeros in 6..7, half 1 zeros
+    // (lanes 32..63 of the split-operand MFMA read it); stored half-major, so
+    // that 8 consecutive rows' reads of one half are 128 contiguous bytes (as
+    // 32-byte rows they were 2-way bank conflicted).  In mixed mode ta holds
+    // fp32 2^-8 s_a in its first BM dwords.
+    uint4 ta[2][2][BM];
+    uint4 tb[2][2][BN];
 };
 
 // Orders this wave's LDS accesses around the workgroup barrier (LDS only:
@@ -218,12 +220,12 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 uint32_t x0, x1, x2;
                 split3(s, x0, x1, x2);
                 // slots 0..5: x0 x0 x0 x1 x1 x2 (paired with y0 y1 y2 y0 y1 y0)
-                sh.ta[buf][ht][0] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
+                sh.ta[buf][0][ht] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
             }
         } else if (has_scale) {
             uint32_t y0, y1, y2;
             split3(rs[set], y0, y1, y2);
-            sh.tb[buf][ht][0] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+            sh.tb[buf][0][ht] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
         }
     };
 
@@ -270,8 +272,8 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             v8bf opa[2], opb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                opa[i] = __builtin_bit_cast(v8bf, sh.ta[buf][wm * 64 + i * 32 + trow][thalf]);
-                opb[i] = __builtin_bit_cast(v8bf, sh.tb[buf][wn * 64 + i * 32 + trow][thalf]);
+                opa[i] = __builtin_bit_cast(v8bf, sh.ta[buf][thalf][wm * 64 + i * 32 + trow]);
+                opb[i] = __builtin_bit_cast(v8bf, sh.tb[buf][thalf][wn * 64 + i * 32 + trow]);
             }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -365,8 +367,8 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     // flight, stage 0 into buffer 0 ---
     if (!MIXED) {
         for (int i = tid; i < 2 * (BM + BN); i += THREADS) {
-            uint4* row = i < 2 * BM ? sh.ta[i / BM][i % BM] : sh.tb[(i - 2 * BM) / BN][(i - 2 * BM) % BN];
-            row[1] = make_uint4(0, 0, 0, 0);
+            if (i < 2 * BM) sh.ta[i / BM][1][i % BM] = make_uint4(0, 0, 0, 0);
+            else sh.tb[(i - 2 * BM) / BN][1][(i - 2 * BM) % BN] = make_uint4(0, 0, 0, 0);
         }
     }
     load_stage(0, 0);
