@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the probes of the GPU's measured ceilings")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per step instead of eager launches "
                          "(eager launches keep the GPU busy here: the host enqueues faster than "
@@ -254,6 +256,39 @@ def write_traffic(prof_dir, workloads):
     print(json.dumps({w: out["workloads"][w]["hbm_bytes_per_launch"] for w in workloads}))
 
 
+def measure_ceilings(torch, apex4):
+    """The GPU's measured ceilings from the library's probes
+    (include/apex4_probe.h): independent int8 MFMAs, a streaming read of
+    2 GiB (past the 256 MB last-level cache), fp32 FMA chains.  Each is the
+    best of 3 runs timed with HIP events on the launch stream."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    isink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        rates = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            work = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rates.append(work / (e0.elapsed_time(e1) * 1e-3))
+        return max(rates)
+
+    out = {"mfma_i8_TOPS": best(lambda: apex4.probe_mfma_i8(2000, isink)) / 1e12,
+           "hbm_read_GBps": best(lambda: apex4.probe_hbm_read(buf, isink)) / 1e9,
+           "valu_f32_TFLOPs": best(lambda: apex4.probe_valu_f32(4000, fsink)) / 1e12,
+           "method": "apex4_probe_* kernels: 4096 waves of independent v_mfma_i32_32x32x32_i8; "
+                     "whole-4KB-row reads of 2 GiB; 8 fp32 FMA chains per thread (no packed fp32)"}
+    del buf
+    return out
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -383,6 +418,11 @@ def main():
                  for (K, N), t, o, b in zip(layers, gemm_ms_avg, layer_ops, bytes_gemm)]
     print(json.dumps({"workload": args.workload, "per_layer": per_layer}), file=sys.stderr)
 
+    ceilings = None if args.no_ceilings else measure_ceilings(torch, apex4)
+    measured = None
+    if ceilings is not None:
+        measured = ceilings["mfma_i8_TOPS"] if bound == "mfma" else ceilings["hbm_read_GBps"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, M, ga, gw, act, args.cpu_rows)
@@ -409,7 +449,10 @@ def main():
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
                      "kernel": "gemm (apex4_gemm_w4a4)",
-                     "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3)},
+                     "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3),
+                     "measured_ceiling": measured,
+                     "frac_of_measured": None if measured is None else achieved / measured},
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

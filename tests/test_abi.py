@@ -1,7 +1,9 @@
-"""CPU-side checks of the C ABI (include/apex4.h): the library loads, exports
-every declared symbol, and rejects bad arguments on the host with the
-documented status codes.  No call here reaches the GPU: every call fails a
+"""CPU-side checks of the C ABI (include/apex4.h, include/apex4_probe.h): the
+library loads, exports every declared symbol, and rejects bad arguments on the
+host with the documented status codes.  No call here reaches the GPU: every call fails a
 host-side check, which runs before any HIP call."""
+import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -11,7 +13,7 @@ import pytest
 from w4a4_group_quantized_amd import apex4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "apex4.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
 A16 = 0x10000          # fake, 16-byte aligned device addresses: never dereferenced
@@ -20,9 +22,12 @@ MIS = 0x10001          # misaligned
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(apex4_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(apex4_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -103,3 +108,17 @@ def test_gemm_validation(L):
     # empty shapes are successful no-ops
     assert _gemm(L, M=0, qa=None, sa=None, y16=None) == OK
     assert _gemm(L, N=0, qw=None, sw=None, y16=None) == OK
+
+
+def test_probe_validation(L):
+    """The probes check their arguments on the host (nothing is launched)."""
+    d = ctypes.c_double(0.0)
+    assert L.apex4_probe_mfma_i8(0, A16, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_mfma_i8(10, None, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_mfma_i8(10, MIS, ctypes.byref(d), None) == ALIGN
+    assert L.apex4_probe_valu_f32(0, A16, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_valu_f32(10, A16, None, None) == INVALID
+    assert L.apex4_probe_hbm_read(A16, 4095, A16b, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_hbm_read(A16, 0, A16b, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_hbm_read(None, 4096, A16b, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_hbm_read(MIS, 4096, A16b, ctypes.byref(d), None) == ALIGN

@@ -19,7 +19,7 @@ OK = 0
 STATUS_NAMES = {0: "APEX4_OK", 1: "APEX4_ERR_INVALID_ARG", 2: "APEX4_ERR_UNSUPPORTED",
                 3: "APEX4_ERR_ALIGNMENT", 4: "APEX4_ERR_WORKSPACE", 5: "APEX4_ERR_HIP"}
 
-# name -> (restype, argtypes); mirrors include/apex4.h
+# name -> (restype, argtypes); mirrors include/apex4.h and include/apex4_probe.h
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -30,6 +30,9 @@ SIGNATURES = {
     "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "apex4_probe_hbm_read": (_I32, [_P, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "apex4_probe_valu_f32": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -141,3 +144,32 @@ def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bo
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16
+
+
+def _probe(name: str, *args):
+    """Run one probe of include/apex4_probe.h on torch's current stream;
+    returns the work it reports (operations or bytes)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = ctypes.c_double(0.0)
+    _check(name, getattr(lib(), name)(*args, ctypes.byref(out), _stream(torch, dev)))
+    return out.value
+
+
+def probe_mfma_i8(iters: int, sink) -> float:
+    """Independent int8 MFMAs; returns the integer operations issued."""
+    _need_gpu(sink, "sink")
+    return _probe("apex4_probe_mfma_i8", iters, _ptr(sink))
+
+
+def probe_hbm_read(buf, sink) -> float:
+    """Streaming read of the whole of `buf` (a multiple of 4096 bytes); returns the bytes read."""
+    _need_gpu(buf, "buf")
+    _need_gpu(sink, "sink")
+    return _probe("apex4_probe_hbm_read", _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink))
+
+
+def probe_valu_f32(iters: int, sink) -> float:
+    """fp32 FMA chains on the vector ALU; returns the floating-point operations."""
+    _need_gpu(sink, "sink")
+    return _probe("apex4_probe_valu_f32", iters, _ptr(sink))

@@ -1,0 +1,118 @@
+// Measurement probes (include/apex4_probe.h): the int8 matrix-unit rate, the
+// HBM read rate and the fp32 vector-ALU rate of the GPU at hand, the ceilings
+// the GEMM kernels are quoted against besides the datasheet peaks.
+#include "apex4_probe.h"
+
+#include <hip/hip_runtime.h>
+
+namespace apex4 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int PROBE_BLOCKS = 1024;
+constexpr int PROBE_THREADS = 256;
+
+// 4 independent accumulators per wave, so that consecutive MFMAs never wait
+// on each other; the operands are lane-dependent values the compiler cannot
+// fold.
+__global__ __launch_bounds__(PROBE_THREADS) void probe_mfma_kernel(int64_t iters, int32_t* sink)
+{
+    const int l = threadIdx.x;
+    const v4i a = v4i{l, 3 * l + 1, 5 * l + 2, 7 * l + 3};
+    const v4i b = v4i{11 * l + 5, 13 * l + 7, 17 * l + 9, 19 * l + 11};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int64_t i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+    }
+    int s = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] ^ c1[r] ^ c2[r] ^ c3[r];
+    if (s == 0x7fffffff) sink[0] = s;
+}
+
+// Every wave reads whole 4 KB rows: lane l takes bytes [64 l, 64 l + 64) of a
+// row as four 16-byte loads, rows dealt round-robin to the waves.
+__global__ __launch_bounds__(PROBE_THREADS) void probe_read_kernel(const uint4* __restrict__ buf, int64_t rows,
+                                                                   int32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * (PROBE_THREADS / 64) + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * (PROBE_THREADS / 64);
+    uint32_t acc = 0;
+    for (int64_t row = gw; row < rows; row += nw) {
+        const uint4* p = buf + row * 256 + 4 * lane;
+        const uint4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
+        acc ^= v0.x ^ v1.y ^ v2.z ^ v3.w;
+        acc += v0.w ^ v1.x ^ v2.y ^ v3.z;
+    }
+    if (acc == 0x7fffffffu) sink[0] = (int32_t)acc;
+}
+
+// 8 independent FMA chains per thread.
+__global__ __launch_bounds__(PROBE_THREADS) void probe_valu_kernel(int64_t iters, float* sink)
+{
+    const float t = (float)threadIdx.x * 1e-3f;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = t + (float)j;
+    const float m = 0.9999f, c = 1e-4f;
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = fmaf(x[j], m, c);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += x[j];
+    if (s == -12345.0f) sink[0] = s;
+}
+
+apex4_status launched()
+{
+    return hipGetLastError() == hipSuccess ? APEX4_OK : APEX4_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+}  // namespace apex4
+
+extern "C" {
+
+apex4_status apex4_probe_mfma_i8(int64_t iters, int32_t* sink, double* ops_out, void* stream)
+{
+    using namespace apex4;
+    if (iters < 1 || sink == nullptr || ops_out == nullptr) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
+    *ops_out = (double)PROBE_BLOCKS * (PROBE_THREADS / 64) * (double)iters * 4 * 2 * 32.0 * 32 * 32;
+    probe_mfma_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
+    return launched();
+}
+
+apex4_status apex4_probe_hbm_read(const void* buf, int64_t bytes, int32_t* sink, double* bytes_out, void* stream)
+{
+    using namespace apex4;
+    if (buf == nullptr || sink == nullptr || bytes_out == nullptr || bytes <= 0 || bytes % 4096 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
+    *bytes_out = (double)bytes;
+    probe_read_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(static_cast<const uint4*>(buf),
+                                                                               bytes / 4096, sink);
+    return launched();
+}
+
+apex4_status apex4_probe_valu_f32(int64_t iters, float* sink, double* flops_out, void* stream)
+{
+    using namespace apex4;
+    if (iters < 1 || sink == nullptr || flops_out == nullptr) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
+    *flops_out = (double)PROBE_BLOCKS * PROBE_THREADS * (double)iters * 8 * 2;
+    probe_valu_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
+    return launched();
+}
+
+}  // extern "C"
