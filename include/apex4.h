@@ -116,6 +116,26 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
                              void* y_f16, float* y_f32, int32_t* psum_dbg,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Granularity selection for a GEMM shape on this GPU (APEX4 page, Abstract:
+ * granularity adaptation by the GPU's matrix-to-vector throughput balance).
+ * The modes, finest first: g = 32, 64, 128; mixed (group_a = 128, group_w =
+ * K); g = 256; per-channel (g = K).  Each mode's time is modelled as
+ *     max(bytes / 5.0e12 B/s,  2*M*N*K / rate(mode)),
+ * bytes = M*K/2 + N*K/2 + 4*(M*K/group_a + N*K/group_w) + 2*M*N, with
+ * rate(mode) the GEMM rate measured on MI355X for that mode (g = 32: 487,
+ * 64: 821, 128: 1495, mixed: 1635, 256: 1528, K: 1882 TOPS), and the finest
+ * mode whose modelled speed is at least min_rel_speed times the fastest
+ * mode's is returned.  Modes whose groups do not divide K are skipped.
+ * Host function: touches no device memory.
+ *   M, N >= 1; K >= 128, K % 128 == 0; 0 < min_rel_speed <= 1.
+ *   group_a, group_w: HOST int32 outputs (group_w == K for per-channel
+ *   weights), valid arguments for apex4_quantize_act / apex4_pack_weight /
+ *   apex4_gemm_w4a4.
+ */
+apex4_status apex4_select_granularity(int64_t M, int64_t N, int64_t K, double min_rel_speed,
+                                      int32_t* group_a, int32_t* group_w);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,8 @@ SIGNATURES = {
     "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
+                                        ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_hbm_read": (_I32, [_P, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_valu_f32": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
@@ -144,6 +146,15 @@ def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bo
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16
+
+
+def select_granularity(M: int, N: int, K: int, min_rel_speed: float = 0.75) -> tuple[int, int]:
+    """(group_a, group_w) from apex4_select_granularity (include/apex4.h): the
+    finest group mode within min_rel_speed of the fastest one for this shape."""
+    ga, gw = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("apex4_select_granularity",
+           lib().apex4_select_granularity(M, N, K, min_rel_speed, ctypes.byref(ga), ctypes.byref(gw)))
+    return ga.value, gw.value
 
 
 def _probe(name: str, *args):
