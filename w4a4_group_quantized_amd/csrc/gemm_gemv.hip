@@ -1,4 +1,4 @@
-// W4A4 GEMM for a few token rows (decode, M <= 4) on gfx950: weight rows
+// W4A4 GEMM for one or two token rows (decode; built for M <= 4) on gfx950: weight rows
 // streamed whole by single waves, INT4 x INT4 products on v_dot8c_i32_i4.
 //
 // With a handful of tokens the product is bound by reading the packed weights
@@ -27,9 +27,10 @@
 // (the first weight loads are issued before that copy, so it overlaps their
 // latency).  Per weight word the lane issues M dot8 and reads M activation
 // words from LDS, so the kernel stays at the weight-streaming rate only for
-// a few rows: at 8 rows the skinny MFMA kernel is faster.  Lane l reads the four 16-byte quads of its unit starting at quad
-// (l >> 1) & 3, for activations and weights alike, so that 8 consecutive
-// lanes hit distinct LDS banks.
+// a few rows: from 3 rows on the LDS-streaming MFMA kernel is faster, and the
+// dispatch sends only 1 or 2 rows here.  Lane l reads the four 16-byte quads
+// of its unit starting at quad (l >> 1) & 3, for activations and weights
+// alike, so that 8 consecutive lanes hit distinct LDS banks.
 #include "internal.h"
 
 namespace apex4 {
