@@ -192,15 +192,17 @@ def test_gemm_groups_of_two_stages(dev, M, N, K, ga, gw):
 
 
 @pytest.mark.parametrize("M,N,K", [(24, 9000, 4224), (64, 9000, 4224), (48, 5000, 2048), (12, 9000, 20480),
-                                   (4, 9000, 36864), (4, 3000, 40960)])
+                                   (4, 9000, 36864), (4, 3000, 40960), (16, 9000, 10240), (8, 5000, 20480),
+                                   (3, 2000, 40960)])
 @pytest.mark.parametrize("ga,gw", [(128, 128), (128, "K")])
 def test_gemm_decode_many_blocks(dev, M, N, K, ga, gw):
     """Decode shapes with several 16-column blocks per workgroup: the K-outer
     kernel with groups of 4 blocks (24 rows, 563 blocks) and of 2 (64 and 48
     rows, the last group half empty at 9000 columns), K = 4224 ending in a
     128-value item; the LDS-streaming kernel with the activation rows brought
-    per item because they do not fit whole (12 rows of K = 20480, 4 rows of
-    K = 40960), and held whole when they just fit (4 rows of K = 36864)."""
+    per item because they do not fit whole (12 rows of K = 20480, 4 and 3
+    rows of K = 40960, 16 rows of K = 10240, 8 rows of K = 20480), and held
+    whole when they just fit (4 rows of K = 36864)."""
     ga = K if ga == "K" else ga
     gw = K if gw == "K" else gw
     x, w = inputs.problem(M, N, K, seed=31 + M, act="outlier")
