@@ -14,15 +14,16 @@ def built():
         pytest.skip("libapex4.so not built (run __graft_entry__.build())")
 
 
-def test_prefill_picks_g128_at_75_percent():
-    # compute-bound: 1495/1882 = 0.79 >= 0.75 > 821/1882 = 0.44
-    assert apex4.select_granularity(2048, 12288, 4096, 0.75) == (128, 128)
+def test_prefill_picks_g128_at_65_percent():
+    # compute-bound: 1507/2231 = 0.675 >= 0.65 > 815/2231 = 0.37
+    assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # mixed 1635/1882 = 0.87 qualifies at 0.85, g=256 (0.81) does not come first
-    assert apex4.select_granularity(8192, 28672, 8192, 0.85) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.9) == (8192, 8192)
+    # mixed 1661/2231 = 0.745 qualifies at 0.72 (g=128, 0.675, does not);
+    # at 0.75 neither mixed nor g=256 (0.686) does
+    assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (128, 8192)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 
 

@@ -38,7 +38,9 @@
 // MFMA over the exact three-piece splits of both scales (six of the nine cross
 // products; the three dropped are below 2^-23 of S).  One group over all of K
 // (per-channel scales) keeps P in the MFMA accumulator through the loop and
-// is rescaled once.  Mixed mode (per-channel weight scales, activation groups
+// is rescaled once; with no rescale to overlap, both wave groups then run the
+// matrix work of every stage together (one barrier per stage: the ping-pong
+// offset would only leave each SIMD's matrix unit with one wave).  Mixed mode (per-channel weight scales, activation groups
 // of 128) rescales with s_a alone and applies s_w in the epilogue.
 #include "internal.h"
 
@@ -290,8 +292,11 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         const uint8_t* la = sh.a[buf] + frag;
         const uint8_t* lb = sh.b[buf] + fragb;
         v4i fa[2][4], fb[2][4];
-        if (zero) {
-            // P starts here: all fragments first
+        // one group over K: P is live across stages but nothing else is, so
+        // the fragments can all be read first as well
+        const bool upfront = zero || SPG == 0;
+        if (upfront) {
+            // all fragments first
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -299,10 +304,12 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                     fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
                     fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
                 }
+            // (one group: every read issued before the first MFMA)
+            if (SPG == 0) __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (!zero) {
+            if (!upfront) {
                 // P is live from the stage before (groups of two stages): the
                 // fragments K-step by K-step (kept apart by scheduling
                 // barriers), fewer registers at once
@@ -392,7 +399,15 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         // end of K read other rows or zeros, and the stores go to a buffer
         // that is no longer read; unconditional memory operations keep the
         // wait counts exact (the loads of stage t+2 stay in flight).
-        if (EARLY) {
+        if (SPG == 0) {
+            // One group over K: no per-stage rescale to overlap, so both wave
+            // groups run the matrix work of every stage at the same time (two
+            // waves per SIMD issuing MFMAs), one barrier per stage.
+            load_stage(t + 2, h);
+            mma_stage(h, zero, ends);
+            store_stage(h ^ 1, h ^ 1);
+            lds_barrier();
+        } else if (EARLY) {
             // phase 1: matrix work of stage t, copy of stage t+1
             load_stage(t + 2, h);
             if (SPG == 2) {
