@@ -58,6 +58,14 @@ WORKLOADS = {
     "sweep-mixed": ("granularity sweep, mixed (per-channel weights, g=128 activations)", 8192,
                     [(8192, 28672)], 128, 8192, "student_t"),
 }
+# Whole-layer workloads (w4a4_group_quantized_amd/linear.py, LlamaLayerW4A4):
+# name -> (description, M, hidden, intermediate)
+LAYER_WORKLOADS = {
+    "llama2-7b-layer-prefill": ("one LLaMA-2-7B-shaped decoder layer's linear path end to end (QKV, O, "
+                                "gate+up, down on each other's outputs; V as the attention stand-in, "
+                                "residual adds and SwiGLU as torch ops), M=2048, g=128", 2048, 4096, 11008),
+    "llama2-7b-layer-decode-m16": ("the same layer at M=16 (decode)", 16, 4096, 11008),
+}
 for _M in (1, 4, 16, 64):
     WORKLOADS[f"llama2-70b-decode-m{_M}"] = (
         f"LLaMA-2-70B-shaped decode, M={_M}: up-proj (K=8192, N=28672) and down-proj "
@@ -69,7 +77,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the GPU's measured ceilings")
@@ -302,6 +310,10 @@ def main():
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in LAYER_WORKLOADS:
+        run_layer(args)
+        return
+
     import torch
     from w4a4_group_quantized_amd import apex4
 
@@ -454,6 +466,103 @@ def main():
                      "frac_of_measured": None if measured is None else achieved / measured},
         "ceilings": ceilings,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def run_layer(args):
+    """Time LlamaLayerW4A4.forward end to end (the four W4A4 linears and the
+    torch ops between them).  value: sum of 2*M*N*K over the four GEMMs /
+    layer time.  Also reported: the time of the W4A4 calls alone (quantize +
+    GEMM of each linear on the inputs it sees in the layer) and the GEMM
+    kernel roofline.  Decode cycles through enough independent layers (>= 1
+    GiB of packed weights) that the weights stream from HBM."""
+    import torch
+    from w4a4_group_quantized_amd import apex4
+    from w4a4_group_quantized_amd.linear import LlamaLayerW4A4
+
+    desc, M, hidden, inter = LAYER_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    apex4.lib()
+    g = 128
+    shapes = [(hidden, 3 * hidden), (hidden, hidden), (hidden, 2 * inter), (inter, hidden)]
+    bound = rl.bound_of(M, shapes[0][1], shapes[0][0], g, g)
+    layer_bytes = sum(rl.gemm_bytes(M, N, K, g, g) for (K, N) in shapes)
+    copies = 1 if bound == "mfma" else max(2, int(np.ceil(2**30 / layer_bytes)))
+    layers = [LlamaLayerW4A4.random(hidden, inter, g, seed=c, device=dev) for c in range(copies)]
+    rng = np.random.default_rng(1000)
+    x = torch.from_numpy(inputs.activations(rng, M, hidden, "outlier", 1000)).to(dev)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        layers[i % copies](x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        layers[s % copies](x)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the W4A4 calls alone, on the inputs each linear sees in the layer
+    _, seen = layers[0](x, return_inputs=True)
+    lins = [[getattr(l, n) for n in LlamaLayerW4A4.NAMES] for l in layers]
+    outs = [y for (_, y) in seen]
+    ins = [xi for (xi, _) in seen]
+    torch.cuda.synchronize()
+    launch = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(launch)
+        for r in range(reps):
+            fn(r)
+        e1.record(launch)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def w4a4_only(r=0):
+        for j, lin in enumerate(lins[r % copies]):
+            lin(ins[j], out=outs[j])
+    w4a4_ms = timed(lambda r=0: w4a4_only(r))
+    # GEMM kernel alone per linear, back-to-back launches on the launch stream
+    acts = [lins[0][j]._act_buffers(ins[j].shape[0], dev) for j in range(4)]
+    gemm_ms = []
+    for j, (K, N) in enumerate(shapes):
+        def gemms(r=0, j=j, K=K):
+            for c in range(max(copies, 4)):
+                lin = lins[(r + c) % copies][j]
+                apex4.gemm(acts[j][0], acts[j][1], g, lin.qw, lin.sw, g, K, y16=outs[j])
+        gemm_ms.append(timed(gemms) / max(copies, 4))
+    ops = sum(rl.gemm_ops(M, N, K) for (K, N) in shapes)
+    if bound == "mfma":
+        achieved, peak, unit = ops / (sum(gemm_ms) * 1e-3) / 1e12, rl.PEAK_INT8_OPS / 1e12, "TFLOP/s"
+    else:
+        achieved, peak, unit = layer_bytes / (sum(gemm_ms) * 1e-3) / 1e9, rl.PEAK_HBM_BYTES / 1e9, "GB/s"
+    out = {
+        "metric": METRIC,
+        "value": ops / (ms_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on i8 MFMA (i32 sums), f32 rescale; fp16 torch ops between the linears",
+        "data": "synthetic",
+        "config": {"workload": desc, "M": M, "hidden": hidden, "intermediate": inter,
+                   "layers_KN": shapes, "group_a": g, "group_w": g, "activations": "outlier",
+                   "timed": "LlamaLayerW4A4.forward (quantize_act + gemm per linear, torch ops between)",
+                   "layers_cycled": copies, "parallelism": "single GPU"},
+        "w4a4_ms_per_step": w4a4_ms,
+        "w4a4_share": w4a4_ms / ms_step,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "gemm (apex4_gemm_w4a4)",
+                     "kernel_avg_us": float(np.mean(gemm_ms) * 1e3)},
     }
     print(json.dumps(out))
 

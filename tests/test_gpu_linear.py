@@ -1,0 +1,105 @@
+"""W4A4Linear and the synthetic LLaMA-shaped layer (w4a4_group_quantized_amd/linear.py)
+against the CPU oracle.
+
+The module runs apex4_quantize_act and apex4_gemm_w4a4; the bar is the one of
+the GEMM parity tests: packed weight codes and scales bit-exact, fp16 output
+within one fp16 ulp (plus 1e-5 of max|Y_ref|) of fp16(Y_ref).  In the layer,
+every linear is checked on the fp16 input it actually received (the torch
+ops between the linears are not part of the method and are not checked
+against the oracle).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import oracle as orc  # noqa: E402
+from w4a4_group_quantized_amd import apex4, inputs  # noqa: E402
+from w4a4_group_quantized_amd.linear import LlamaLayerW4A4, W4A4Linear  # noqa: E402
+
+REL_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    apex4.lib()   # raises when the HIP library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def check_y16(y16, r32):
+    tol = REL_TOL * max(float(np.abs(r32).max()), 1e-30)
+    r16 = r32.astype(np.float16)
+    ulp = np.spacing(np.abs(r16)).astype(np.float64)
+    d16 = np.abs(y16.astype(np.float64) - r16.astype(np.float64))
+    assert np.all(d16 <= ulp + tol), float((d16 / (ulp + tol)).max())
+
+
+def oracle_linear(x, w, ga, gw):
+    K = x.shape[1]
+    qa, sa = orc.quantize(x, ga)
+    qw, sw = orc.quantize(w, gw)
+    _, r32, _ = orc.gemm(qa, sa, ga, qw, sw, gw, K)
+    return qw, sw, r32
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,ga,gw", [(37, 512, 384, 128, 128), (5, 1024, 256, 128, 1024),
+                                         (64, 768, 640, 64, 64)])
+def test_linear_matches_oracle(dev, M, K, N, ga, gw):
+    x, w = inputs.problem(M, N, K, seed=M + K, act="outlier")
+    lin = W4A4Linear.from_weight(torch.from_numpy(w).to(dev), gw, ga)
+    y = lin(torch.from_numpy(x).to(dev))
+    y2 = lin(torch.from_numpy(x).to(dev))          # buffers reused at the same row count
+    torch.cuda.synchronize()
+    qw, sw, r32 = oracle_linear(x, w, ga, gw)
+    assert np.array_equal(lin.qw.cpu().numpy(), qw)
+    assert np.array_equal(lin.sw.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    check_y16(y.cpu().numpy(), r32)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.gpu
+def test_linear_leading_dims_and_new_row_counts(dev):
+    x, w = inputs.problem(2 * 7, 256, 512, seed=11, act="normal")
+    lin = W4A4Linear.from_weight(torch.from_numpy(w).to(dev), 128)
+    tx = torch.from_numpy(x).to(dev)
+    y3 = lin(tx.view(2, 7, 512))
+    assert y3.shape == (2, 7, 256)
+    y1 = lin(tx[:3])                                 # another row count: its own buffers
+    torch.cuda.synchronize()
+    _, _, r32 = oracle_linear(x, w, 128, 128)
+    check_y16(y3.reshape(14, 256).cpu().numpy(), r32)
+    check_y16(y1.cpu().numpy(), r32[:3])
+    with pytest.raises(ValueError):
+        lin(tx[:, :256])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [40, 3])
+def test_layer_every_linear_matches_oracle(dev, M):
+    hidden, inter, g = 256, 384, 128
+    layer = LlamaLayerW4A4.random(hidden, inter, g, seed=3, device=dev)
+    # the same weights, regenerated on the host in the same draw order
+    rng = np.random.default_rng(3)
+    shapes = {"qkv": (3 * hidden, hidden), "o": (hidden, hidden),
+              "gate_up": (2 * inter, hidden), "down": (hidden, inter)}
+    ws = {n: inputs.weights(rng, *shapes[n]) for n in LlamaLayerW4A4.NAMES}
+    x = inputs.activations(np.random.default_rng(7), M, hidden, "outlier", 7)
+    out, seen = layer(torch.from_numpy(x).to(dev), return_inputs=True)
+    torch.cuda.synchronize()
+    assert out.shape == (M, hidden) and bool(torch.isfinite(out).all())
+    for name, (xi, yi) in zip(LlamaLayerW4A4.NAMES, seen):
+        qw, _, r32 = oracle_linear(xi.cpu().numpy(), ws[name], g, g)
+        assert np.array_equal(getattr(layer, name).qw.cpu().numpy(), qw), name
+        check_y16(yi.cpu().numpy(), r32)
+    assert layer.linear_shapes() == [(256, 768), (256, 256), (256, 768), (384, 256)]
+
+
+def test_linear_refuses_host_tensors():
+    """No CPU path: the module takes GPU-packed weights only (host logic, no GPU needed)."""
+    qw = torch.zeros((8, 64), dtype=torch.uint8)
+    sw = torch.ones((8, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        W4A4Linear(qw, sw, 128)
