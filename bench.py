@@ -494,12 +494,29 @@ def run_layer(args):
     x = torch.from_numpy(inputs.activations(rng, M, hidden, "outlier", 1000)).to(dev)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, copies)):
         layers[i % copies](x)
     torch.cuda.synchronize()
+    # --graph: each layer's forward captured once as a HIP graph (the library
+    # allocates and clears nothing itself, so its launches capture as they are)
+    graphs = None
+    if args.graph:
+        cap = torch.cuda.Stream()
+        graphs = []
+        for c in range(copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                layers[c](x)
+            graphs.append(gr)
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        layers[s % copies](x)
+        if graphs is None:
+            layers[s % copies](x)
+        else:
+            graphs[s % copies].replay()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
@@ -525,7 +542,16 @@ def run_layer(args):
     def w4a4_only(r=0):
         for j, lin in enumerate(lins[r % copies]):
             lin(ins[j], out=outs[j])
-    w4a4_ms = timed(lambda r=0: w4a4_only(r))
+    if graphs is None:
+        w4a4_ms = timed(lambda r=0: w4a4_only(r))
+    else:
+        wgraphs = []
+        for c in range(copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                w4a4_only(c)
+            wgraphs.append(gr)
+        w4a4_ms = timed(lambda r=0: wgraphs[r % copies].replay(), reps=max(5, copies))
     # GEMM kernel alone per linear, back-to-back launches on the launch stream
     acts = [lins[0][j]._act_buffers(ins[j].shape[0], dev) for j in range(4)]
     gemm_ms = []
@@ -556,6 +582,7 @@ def run_layer(args):
         "config": {"workload": desc, "M": M, "hidden": hidden, "intermediate": inter,
                    "layers_KN": shapes, "group_a": g, "group_w": g, "activations": "outlier",
                    "timed": "LlamaLayerW4A4.forward (quantize_act + gemm per linear, torch ops between)",
+                   "launch": "eager" if graphs is None else "HIP graph per layer forward",
                    "layers_cycled": copies, "parallelism": "single GPU"},
         "w4a4_ms_per_step": w4a4_ms,
         "w4a4_share": w4a4_ms / ms_step,

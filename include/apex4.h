@@ -83,7 +83,14 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
 
 /*
  * Bytes of device workspace apex4_gemm_w4a4 needs for this shape (host
- * function).  Currently 0 for every shape; callers should still ask.
+ * function; it reads the current device's compute-unit count).  Nonzero only
+ * where the compute-bound kernel (groups of 128, M > 64) would leave its last
+ * round of output tiles at most half the GPU's compute units: those tiles then
+ * run as two halves of K into fp32 partial tiles in the workspace (2 x tiles
+ * x 256 x 128 x 4 bytes, e.g. 25.2 MB for M = 2048, N = 22016 on 256 CUs) and
+ * a reduction adds the halves in a fixed order.  0 for invalid or empty
+ * shapes.  The workspace holds nothing between calls; calls that overlap on
+ * one workspace race.
  */
 size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a,
                                  int32_t group_w);
@@ -103,7 +110,8 @@ size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
  *   y_f32  [M, N] fp32 output before the fp16 rounding, or NULL.
  *   psum_dbg [M, N, G] int32 per-group sums P_j, or NULL (debug; slow).
  *   workspace / workspace_bytes: at least apex4_gemm_workspace_size() bytes
- *   (NULL allowed when that is 0).
+ *   (NULL allowed when that is 0), 16-byte aligned; device memory owned by the
+ *   caller, overwritten by the call.
  * Sizes: M >= 0, N >= 0 (either 0 is a no-op), K > 0, K % 128 == 0,
  *   group_a in {32, 64, 128, 256} or group_a == K, and either
  *   group_w == group_a, or group_w == K (mixed granularity: per-channel

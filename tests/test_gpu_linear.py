@@ -103,3 +103,24 @@ def test_linear_refuses_host_tensors():
     sw = torch.ones((8, 1), dtype=torch.float32)
     with pytest.raises(ValueError):
         W4A4Linear(qw, sw, 128)
+
+
+@pytest.mark.gpu
+def test_layer_graph_replays_match_eager(dev):
+    """The layer forward captured as one HIP graph: every replay, with eager
+    work and synchronizations between them, gives the eager result bit for bit."""
+    layer = LlamaLayerW4A4.random(256, 384, 128, seed=5, device=dev)
+    x = torch.from_numpy(inputs.activations(np.random.default_rng(9), 16, 256, "outlier", 9)).to(dev)
+    ref = layer(x).clone()                      # eager (also allocates the activation buffers)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        out = layer(x)
+    for r in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        other = layer(x * 0.5)                  # eager work on the same buffers between replays
+        torch.cuda.synchronize()
+        assert not torch.equal(other, ref)

@@ -292,3 +292,44 @@ def test_full_70b_prefill(dev, K, N):
 def test_full_granularity_sweep(dev, ga, gw):
     x, w = big_problem(8192, 28672, 8192, "student_t")
     run_case(dev, x, w, ga, gw, rows=sample_rows(8192, n=8))
+
+
+# ------------------------------------------------- K split of a partial last round
+
+
+@pytest.mark.parametrize("M,N,K,ga,gw", [(300, 16640, 512, 128, 128), (257, 16512, 1152, 128, 128),
+                                         (300, 16640, 1024, 128, 1024)])
+def test_gemm_split_last_round(dev, M, N, K, ga, gw):
+    """Shapes whose last round of 256x128 output tiles fills at most half the
+    GPU's compute units: those tiles run as two K halves into the workspace
+    (odd stage counts split unevenly) and a reduction writes their Y.  Rows
+    of the split tiles and of the others are checked; on a GPU where the
+    shape does not split the test still checks the result."""
+    x, w = inputs.problem(M, N, K, seed=M + N, act="outlier")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // 256) * -(-N // 128)
+    ws = apex4.workspace_size(M, N, K, ga, gw)
+    tail = tiles % cus if tiles > cus else 0
+    if tail and 2 * tail <= cus:
+        assert ws == 2 * tail * 256 * 128 * 4
+    else:
+        assert ws == 0
+    rows = np.unique(np.concatenate([sample_rows(M, n=8), np.arange(M - 3, M), np.arange(256, min(M, 259))]))
+    run_case(dev, x, w, ga, gw, rows=rows)
+
+
+def test_gemm_split_workspace_too_small(dev):
+    M, N, K = 300, 16640, 512
+    need = apex4.workspace_size(M, N, K, 128, 128)
+    if need == 0:
+        pytest.skip("this GPU's compute-unit count does not split the shape")
+    qa = torch.zeros((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.ones((M, K // 128), dtype=torch.float32, device=dev)
+    qw = torch.zeros((N, K // 2), dtype=torch.uint8, device=dev)
+    sw = torch.ones((N, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=dev)
+    st = apex4.lib().apex4_gemm_w4a4(apex4._ptr(qa), apex4._ptr(sa), 128, apex4._ptr(qw), apex4._ptr(sw), 128,
+                                     M, N, K, apex4._ptr(y), None, None, apex4._ptr(ws), need - 16,
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == 4   # APEX4_ERR_WORKSPACE, nothing launched

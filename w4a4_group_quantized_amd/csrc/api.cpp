@@ -65,7 +65,19 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
                                             static_cast<hipStream_t>(stream)));
 }
 
-size_t apex4_gemm_workspace_size(int64_t, int64_t, int64_t, int32_t, int32_t) { return 0; }
+size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w)
+{
+    // shapes apex4_gemm_w4a4 rejects, or that launch nothing, need none
+    if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0) return 0;
+    if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return 0;
+    apex4::GemmProblem p{};
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.ga = group_a;
+    p.gw = group_w;
+    return apex4::gemm_workspace_bytes(p);
+}
 
 apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_a,
                              const void* qw_u8, const float* s_w, int32_t group_w, int64_t M,
@@ -85,7 +97,7 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
     if (M == 0 || N == 0) return APEX4_OK;
     if (!qa_u8 || !s_a || !qw_u8 || !s_w || !y_f16) return APEX4_ERR_INVALID_ARG;
     if (!aligned(qa_u8, 16) || !aligned(qw_u8, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) ||
-        !aligned(y_f16, 2) || !aligned(y_f32, 4) || !aligned(psum_dbg, 4))
+        !aligned(y_f16, 2) || !aligned(y_f32, 4) || !aligned(psum_dbg, 4) || !aligned(workspace, 16))
         return APEX4_ERR_ALIGNMENT;
 
     apex4::GemmProblem p;
@@ -101,6 +113,8 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
     p.y16 = y_f16;
     p.y32 = y_f32;
     p.psum = psum_dbg;
+    p.ws = workspace;
+    p.ws_bytes = workspace_bytes;
     return to_status(apex4::launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
 

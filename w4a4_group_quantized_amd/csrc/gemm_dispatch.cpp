@@ -10,6 +10,24 @@
 
 namespace apex4 {
 
+size_t gemm_workspace_bytes(const GemmProblem& p)
+{
+    // mirrors the order of launch_gemm: only the ping-pong kernel uses one
+    if (p.M <= 2 && gemv_supports(p)) return 0;
+#ifndef APEX4_NO_STREAM
+    if (stream_supports(p)) return 0;
+#endif
+    if (gemv_supports(p)) return 0;
+#ifndef APEX4_NO_KOUTER
+    if (kouter_supports(p)) return 0;
+#endif
+    if (skinny_supports(p)) return 0;
+#ifndef APEX4_NO_PINGPONG
+    if (pingpong_supports(p)) return pingpong_split(p).bytes;
+#endif
+    return 0;
+}
+
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
 {
     if (p.M <= 2 && gemv_supports(p)) return launch_gemm_gemv(p, stream);

@@ -75,6 +75,17 @@ struct PPArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    // Tiles: BM x BN blocks of Y in row-major order over the tile grid;
+    // workgroup b of a launch takes tile tile0 + b (full K, the epilogue
+    // writes Y) or, in a K-split launch (part != null), tile tile0 + b % ntail
+    // over K part b / ntail (stages [0, ksplit) or [ksplit, K/128)), writing
+    // its fp32 sums to part[b / ntail][b % ntail] ([BM][BN], before s_w in
+    // mixed mode) for the reduction kernel.
+    int tiles_n;       // tiles along N: ceil(N / BN)
+    int tile0;
+    int ntail;
+    int ksplit;
+    float* part;
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes)
@@ -159,9 +170,18 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;      // 64-row, 64-column sub-tile
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    int lin = blockIdx.x, kpart = 0;
+    if (a.part) {
+        kpart = lin / a.ntail;
+        lin -= kpart * a.ntail;
+    }
+    const int tile = a.tile0 + lin;
+    const int by = tile / a.tiles_n, bx = tile - by * a.tiles_n;
+    const int m0 = by * BM, n0 = bx * BN;
     const uint32_t rowbytes = (uint32_t)a.K / 2;
-    const int stages = a.K / KSTAGE;
+    // this workgroup's stages: s0 .. s0 + stages - 1
+    const int s0 = kpart ? a.ksplit : 0;
+    const int stages = !a.part ? a.K / KSTAGE : kpart ? a.K / KSTAGE - a.ksplit : a.ksplit;
     const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
     // Per-workgroup buffers: rows past M (N) lie past the end and read zeros.
     // The per-stage offset goes into the scalar offset of the load.
@@ -196,11 +216,12 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     auto load_stage = [&](int t, int set) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], t * ROWB, 0);
+            const u32x4 v =
+                __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], (s0 + t) * ROWB, 0);
             rq[set][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
         // the scale of the group that stage t belongs to
-        const int g = (SPG == 1 ? t : SPG == 2 ? t >> 1 : 0) * 4;
+        const int g = (SPG == 1 ? s0 + t : SPG == 2 ? (s0 + t) >> 1 : 0) * 4;
         if (EARLY || !MIXED)
             rs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g, 0));
     };
@@ -451,6 +472,20 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         rescale(a.G - 1);
     }
 
+    if (a.part) {
+        // K-split part: the tile's fp32 sums, all BM x BN of them
+        float* out = a.part + (size_t)(kpart * a.ntail + lin) * (BM * BN);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    out[(wm * 64 + mt * 32 + acc_row(r, lane)) * BN + wn * 64 + nt * 32 + (lane & 31)] =
+                        acc[mt][nt][r];
+        return;
+    }
+
     // --- epilogue: (mixed: x s_w[n]) -> fp16 (RNE) and optional fp32 ---
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -486,15 +521,100 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_pp_kernel(PPArgs a)
         pp_body<MIXED, DEBUG_P, SPG, false>(a, sh);
 }
 
-template <bool MIXED, int SPG>
-void launch_pp(const PPArgs& t, hipStream_t stream)
+// Y of the K-split tiles: part 0 + part 1 (in that order), then as the
+// epilogue above (mixed: x s_w[n]; fp16 is the RNE rounding of the fp32
+// value).  One thread per 4 consecutive columns of a tile row.
+template <bool MIXED>
+__global__ __launch_bounds__(256) void pp_split_reduce_kernel(PPArgs a)
 {
-    const dim3 grid((t.N + BN - 1) / BN, (t.M + BM - 1) / BM);
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    constexpr int PER_TILE = BM * BN / 4;
+    if (idx >= a.ntail * PER_TILE) return;
+    const int lin = idx / PER_TILE, rem = idx - lin * PER_TILE;
+    const int row = rem / (BN / 4), col = (rem - row * (BN / 4)) * 4;
+    const int tile = a.tile0 + lin;
+    const int by = tile / a.tiles_n, bx = tile - by * a.tiles_n;
+    const int m = by * BM + row;
+    if (m >= a.M) return;
+    const size_t o0 = (size_t)lin * (BM * BN) + row * BN + col;
+    const float4 p0 = *reinterpret_cast<const float4*>(a.part + o0);
+    const float4 p1 = *reinterpret_cast<const float4*>(a.part + (size_t)a.ntail * (BM * BN) + o0);
+    const float s[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = bx * BN + col + j;
+        if (n < a.N) {
+            float v = MIXED ? s[j] * a.sw[n] : s[j];
+            asm volatile("" : "+v"(v));
+            const int64_t o = (int64_t)m * a.N + n;
+            a.y16[o] = (_Float16)v;
+            if (a.y32) a.y32[o] = v;
+        }
+    }
+}
+
+template <bool MIXED, int SPG>
+void launch_pp(const PPArgs& t, int grid, hipStream_t stream)
+{
     if (t.psum) gemm_pp_kernel<MIXED, true, SPG><<<grid, THREADS, 0, stream>>>(t);
     else gemm_pp_kernel<MIXED, false, SPG><<<grid, THREADS, 0, stream>>>(t);
 }
 
+template <bool MIXED, int SPG>
+void launch_pp_all(const PPArgs& t, const PingpongSplit& sp, hipStream_t stream)
+{
+    if (sp.tail == 0) {
+        launch_pp<MIXED, SPG>(t, sp.tiles, stream);
+        return;
+    }
+    // the full rounds of tiles over all of K, then the last (partial) round
+    // as two K halves on twice the workgroups, then their sums
+    PPArgs m = t;
+    launch_pp<MIXED, SPG>(m, sp.tiles - sp.tail, stream);
+    PPArgs k = t;
+    k.tile0 = sp.tiles - sp.tail;
+    k.ntail = sp.tail;
+    k.ksplit = sp.ksplit;
+    k.part = sp.part;
+    launch_pp<MIXED, SPG>(k, 2 * sp.tail, stream);
+    pp_split_reduce_kernel<MIXED><<<(sp.tail * (BM * BN / 4) + 255) / 256, 256, 0, stream>>>(k);
+}
+
+int cu_count()
+{
+    // compute units of the current device (cached per device)
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 }  // namespace
+
+PingpongSplit pingpong_split(const GemmProblem& p)
+{
+    // One workgroup per CU (the LDS of one fills a CU), so a launch runs in
+    // rounds of `cus` tiles.  When the last round is at most half full, its
+    // tiles are split in two over K (at a group boundary: groups of one
+    // stage only), which fills up to twice as many CUs for half as long.
+    PingpongSplit sp;
+    sp.tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int gs = p.ga < p.gw ? p.ga : p.gw;
+    const int cus = cu_count();
+    const int stages = p.K / KSTAGE;
+    if (gs != KSTAGE || stages < 2 || cus <= 0 || sp.tiles <= cus) return sp;
+    const int tail = sp.tiles % cus;
+    if (tail == 0 || 2 * tail > cus) return sp;
+    sp.tail = tail;
+    sp.ksplit = stages / 2;
+    sp.bytes = (size_t)2 * tail * BM * BN * sizeof(float);
+    return sp;
+}
 
 bool pingpong_supports(const GemmProblem& p)
 {
@@ -528,13 +648,22 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
     t.psum = p.psum;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.tile0 = 0;
+    t.ntail = 0;
+    t.ksplit = 0;
+    t.part = nullptr;
+    PingpongSplit sp = pingpong_split(p);
+    // the K split needs its workspace, and is not used for the debug sums
+    if (sp.tail && (p.psum || !p.ws || p.ws_bytes < sp.bytes)) sp.tail = 0;
+    sp.part = static_cast<float*>(p.ws);
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     // mixed mode here: ga = 128 or 256 (the activation groups are 1 or 2 stages)
-    if (mixed && t.spg == 1) launch_pp<true, 1>(t, stream);
-    else if (mixed) launch_pp<true, 2>(t, stream);
-    else if (t.spg == 1) launch_pp<false, 1>(t, stream);
-    else if (gs == p.K) launch_pp<false, 0>(t, stream);
-    else launch_pp<false, 2>(t, stream);
+    if (mixed && t.spg == 1) launch_pp_all<true, 1>(t, sp, stream);
+    else if (mixed) launch_pp_all<true, 2>(t, sp, stream);
+    else if (t.spg == 1) launch_pp_all<false, 1>(t, sp, stream);
+    else if (gs == p.K) launch_pp_all<false, 0>(t, sp, stream);
+    else launch_pp_all<false, 2>(t, sp, stream);
     return hipGetLastError();
 }
 

@@ -21,7 +21,26 @@ struct GemmProblem {
     void* y16;            // fp16 [M, N]
     float* y32;           // fp32 [M, N] or null
     int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
+    void* ws;             // device workspace (gemm_workspace_bytes) or null
+    size_t ws_bytes;
 };
+
+// The ping-pong kernel's K split of a partial last round of tiles: `tail`
+// tiles (0: no split) run as two halves of K (stages [0, ksplit) and
+// [ksplit, K/128)) into an fp32 workspace of `bytes`, then a reduction
+// writes their Y.
+struct PingpongSplit {
+    int tiles = 0;
+    int tail = 0;
+    int ksplit = 0;
+    size_t bytes = 0;
+    float* part = nullptr;
+};
+PingpongSplit pingpong_split(const GemmProblem& p);
+
+// Device workspace the call needs (0 for most shapes): the kernel choice of
+// launch_gemm, shapes only.
+size_t gemm_workspace_bytes(const GemmProblem& p);
 
 // Picks the kernel for the shape: the row-streaming dot8 kernel (M <= 2), the
 // LDS-streaming MFMA kernels (M <= 16, and 17..64 with K outside the column
