@@ -42,6 +42,13 @@
 // matrix work of every stage together (one barrier per stage: the ping-pong
 // offset would only leave each SIMD's matrix unit with one wave).  Mixed mode (per-channel weight scales, activation groups
 // of 128) rescales with s_a alone and applies s_w in the epilogue.
+//
+// Rounds of tiles.  One workgroup fills a CU, so a launch runs in rounds of
+// one tile per CU.  A last round that would leave more than half the CUs
+// idle (e.g. 96 of 256) is run as two halves of K instead (groups of one
+// stage, split at a group boundary) on twice the workgroups; their fp32 tile
+// sums go to the caller's workspace and a small kernel adds the two halves in
+// a fixed order and writes Y as the epilogue does.
 #include "internal.h"
 
 namespace apex4 {
