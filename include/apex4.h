@@ -84,13 +84,14 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
 /*
  * Bytes of device workspace apex4_gemm_w4a4 needs for this shape (host
  * function; it reads the current device's compute-unit count).  Nonzero only
- * where the compute-bound kernel (groups of 128, M > 64) would leave its last
- * round of output tiles at most half the GPU's compute units: those tiles then
- * run as two halves of K into fp32 partial tiles in the workspace (2 x tiles
- * x 256 x 128 x 4 bytes, e.g. 25.2 MB for M = 2048, N = 22016 on 256 CUs) and
- * a reduction adds the halves in a fixed order.  0 for invalid or empty
- * shapes.  The workspace holds nothing between calls; calls that overlap on
- * one workspace race.
+ * where the compute-bound kernel (groups of 128, M > 64, K >= 512) would leave
+ * its last round of 256 x 128 output tiles (its only one, for few tiles) at
+ * most half the GPU's compute units: those tiles then run as P = min(CUs /
+ * tiles, K / 256, 4) parts of K into fp32 partial tiles in the workspace
+ * (P x tiles x 256 x 128 x 4 bytes, e.g. 25.2 MB for M = 2048, N = 22016 on
+ * 256 CUs) and a reduction adds the parts in a fixed order.  0 for invalid or
+ * empty shapes.  The workspace holds nothing between calls; calls that
+ * overlap on one workspace race.
  */
 size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a,
                                  int32_t group_w);

@@ -298,20 +298,24 @@ def test_full_granularity_sweep(dev, ga, gw):
 
 
 @pytest.mark.parametrize("M,N,K,ga,gw", [(300, 16640, 512, 128, 128), (257, 16512, 1152, 128, 128),
-                                         (300, 16640, 1024, 128, 1024)])
+                                         (300, 16640, 1024, 128, 1024), (130, 1000, 4096, 128, 128),
+                                         (300, 4096, 1024, 128, 128), (65, 640, 2048, 128, 2048)])
 def test_gemm_split_last_round(dev, M, N, K, ga, gw):
-    """Shapes whose last round of 256x128 output tiles fills at most half the
-    GPU's compute units: those tiles run as two K halves into the workspace
-    (odd stage counts split unevenly) and a reduction writes their Y.  Rows
-    of the split tiles and of the others are checked; on a GPU where the
-    shape does not split the test still checks the result."""
+    """Shapes whose last round of 256x128 output tiles (the only one, for few
+    tiles) fills at most half the GPU's compute units: those tiles run as 2 to
+    4 parts of K into the workspace (uneven parts when the stage count does
+    not divide: K = 1152 is 9 stages) and a reduction writes their Y.  Rows of
+    the split tiles and of the others are checked; on a GPU where the shape
+    does not split the test still checks the result."""
     x, w = inputs.problem(M, N, K, seed=M + N, act="outlier")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     tiles = -(-M // 256) * -(-N // 128)
+    stages = K // 128
     ws = apex4.workspace_size(M, N, K, ga, gw)
-    tail = tiles % cus if tiles > cus else 0
-    if tail and 2 * tail <= cus:
-        assert ws == 2 * tail * 256 * 128 * 4
+    tail = tiles % cus
+    if tail and 2 * tail <= cus and stages >= 4:
+        parts = min(cus // tail, stages // 2, 4)
+        assert ws == parts * tail * 256 * 128 * 4
     else:
         assert ws == 0
     rows = np.unique(np.concatenate([sample_rows(M, n=8), np.arange(M - 3, M), np.arange(256, min(M, 259))]))

@@ -45,10 +45,11 @@
 //
 // Rounds of tiles.  One workgroup fills a CU, so a launch runs in rounds of
 // one tile per CU.  A last round that would leave more than half the CUs
-// idle (e.g. 96 of 256) is run as two halves of K instead (groups of one
-// stage, split at a group boundary) on twice the workgroups; their fp32 tile
-// sums go to the caller's workspace and a small kernel adds the two halves in
-// a fixed order and writes Y as the epilogue does.
+// idle (e.g. 96 of 256, or a call with only a few tiles) is run as 2 to 4
+// parts of K instead (groups of one stage, split at group boundaries) on as
+// many times the workgroups; their fp32 tile sums go to the caller's
+// workspace and a small kernel adds the parts in a fixed order and writes Y
+// as the epilogue does.
 #include "internal.h"
 
 namespace apex4 {
@@ -85,13 +86,13 @@ struct PPArgs {
     // Tiles: BM x BN blocks of Y in row-major order over the tile grid;
     // workgroup b of a launch takes tile tile0 + b (full K, the epilogue
     // writes Y) or, in a K-split launch (part != null), tile tile0 + b % ntail
-    // over K part b / ntail (stages [0, ksplit) or [ksplit, K/128)), writing
-    // its fp32 sums to part[b / ntail][b % ntail] ([BM][BN], before s_w in
-    // mixed mode) for the reduction kernel.
+    // over K part q = b / ntail of nparts (stages [q S / nparts, (q+1) S /
+    // nparts) of the S = K/128), writing its fp32 sums to part[q][b % ntail]
+    // ([BM][BN], before s_w in mixed mode) for the reduction kernel.
     int tiles_n;       // tiles along N: ceil(N / BN)
     int tile0;
     int ntail;
-    int ksplit;
+    int nparts;
     float* part;
 };
 
@@ -187,8 +188,9 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const int m0 = by * BM, n0 = bx * BN;
     const uint32_t rowbytes = (uint32_t)a.K / 2;
     // this workgroup's stages: s0 .. s0 + stages - 1
-    const int s0 = kpart ? a.ksplit : 0;
-    const int stages = !a.part ? a.K / KSTAGE : kpart ? a.K / KSTAGE - a.ksplit : a.ksplit;
+    const int all_stages = a.K / KSTAGE;
+    const int s0 = a.part ? kpart * all_stages / a.nparts : 0;
+    const int stages = a.part ? (kpart + 1) * all_stages / a.nparts - s0 : all_stages;
     const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
     // Per-workgroup buffers: rows past M (N) lie past the end and read zeros.
     // The per-stage offset goes into the scalar offset of the load.
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_pp_kernel(PPArgs a)
         pp_body<MIXED, DEBUG_P, SPG, false>(a, sh);
 }
 
-// Y of the K-split tiles: part 0 + part 1 (in that order), then as the
+// Y of the K-split tiles: the parts' sums added in part order, then as the
 // epilogue above (mixed: x s_w[n]; fp16 is the RNE rounding of the fp32
 // value).  One thread per 4 consecutive columns of a tile row.
 template <bool MIXED>
@@ -544,9 +546,16 @@ __global__ __launch_bounds__(256) void pp_split_reduce_kernel(PPArgs a)
     const int m = by * BM + row;
     if (m >= a.M) return;
     const size_t o0 = (size_t)lin * (BM * BN) + row * BN + col;
+    const size_t stride = (size_t)a.ntail * (BM * BN);
     const float4 p0 = *reinterpret_cast<const float4*>(a.part + o0);
-    const float4 p1 = *reinterpret_cast<const float4*>(a.part + (size_t)a.ntail * (BM * BN) + o0);
-    const float s[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+    float s[4] = {p0.x, p0.y, p0.z, p0.w};
+    for (int q = 1; q < a.nparts; ++q) {
+        const float4 pq = *reinterpret_cast<const float4*>(a.part + q * stride + o0);
+        s[0] += pq.x;
+        s[1] += pq.y;
+        s[2] += pq.z;
+        s[3] += pq.w;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = bx * BN + col + j;
@@ -575,15 +584,14 @@ void launch_pp_all(const PPArgs& t, const PingpongSplit& sp, hipStream_t stream)
         return;
     }
     // the full rounds of tiles over all of K, then the last (partial) round
-    // as two K halves on twice the workgroups, then their sums
-    PPArgs m = t;
-    launch_pp<MIXED, SPG>(m, sp.tiles - sp.tail, stream);
+    // as nparts K parts on nparts times the workgroups, then their sums
+    if (sp.tiles > sp.tail) launch_pp<MIXED, SPG>(t, sp.tiles - sp.tail, stream);
     PPArgs k = t;
     k.tile0 = sp.tiles - sp.tail;
     k.ntail = sp.tail;
-    k.ksplit = sp.ksplit;
+    k.nparts = sp.nparts;
     k.part = sp.part;
-    launch_pp<MIXED, SPG>(k, 2 * sp.tail, stream);
+    launch_pp<MIXED, SPG>(k, sp.nparts * sp.tail, stream);
     pp_split_reduce_kernel<MIXED><<<(sp.tail * (BM * BN / 4) + 255) / 256, 256, 0, stream>>>(k);
 }
 
@@ -606,20 +614,27 @@ int cu_count()
 PingpongSplit pingpong_split(const GemmProblem& p)
 {
     // One workgroup per CU (the LDS of one fills a CU), so a launch runs in
-    // rounds of `cus` tiles.  When the last round is at most half full, its
-    // tiles are split in two over K (at a group boundary: groups of one
-    // stage only), which fills up to twice as many CUs for half as long.
+    // rounds of `cus` tiles.  When the last round (the only one, for few
+    // tiles) is at most half full, its tiles are split over K into
+    // nparts = min(cus / tiles, stages / 2, 4) parts (at group boundaries:
+    // groups of one stage only), which fills up to nparts times as many CUs
+    // for 1/nparts of the time; the reduction reads nparts partial tiles
+    // (more parts measured slower: their fp32 partial tiles cost more traffic
+    // than the shorter K saves).
     PingpongSplit sp;
     sp.tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     const int gs = p.ga < p.gw ? p.ga : p.gw;
     const int cus = cu_count();
     const int stages = p.K / KSTAGE;
-    if (gs != KSTAGE || stages < 2 || cus <= 0 || sp.tiles <= cus) return sp;
+    if (gs != KSTAGE || stages < 4 || cus <= 0) return sp;
     const int tail = sp.tiles % cus;
     if (tail == 0 || 2 * tail > cus) return sp;
+    int parts = cus / tail;
+    if (parts > stages / 2) parts = stages / 2;
+    if (parts > 4) parts = 4;
     sp.tail = tail;
-    sp.ksplit = stages / 2;
-    sp.bytes = (size_t)2 * tail * BM * BN * sizeof(float);
+    sp.nparts = parts;
+    sp.bytes = (size_t)parts * tail * BM * BN * sizeof(float);
     return sp;
 }
 
@@ -658,7 +673,7 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.tiles_n = (p.N + BN - 1) / BN;
     t.tile0 = 0;
     t.ntail = 0;
-    t.ksplit = 0;
+    t.nparts = 1;
     t.part = nullptr;
     PingpongSplit sp = pingpong_split(p);
     // the K split needs its workspace, and is not used for the debug sums

@@ -25,14 +25,13 @@ struct GemmProblem {
     size_t ws_bytes;
 };
 
-// The ping-pong kernel's K split of a partial last round of tiles: `tail`
-// tiles (0: no split) run as two halves of K (stages [0, ksplit) and
-// [ksplit, K/128)) into an fp32 workspace of `bytes`, then a reduction
-// writes their Y.
+// The ping-pong kernel's K split of a partial last round of tiles: the last
+// `tail` tiles (0: no split) run as `nparts` parts of K into an fp32
+// workspace of `bytes`, then a reduction writes their Y.
 struct PingpongSplit {
     int tiles = 0;
     int tail = 0;
-    int ksplit = 0;
+    int nparts = 1;
     size_t bytes = 0;
     float* part = nullptr;
 };
