@@ -214,7 +214,11 @@ def write_traffic(prof_dir, workloads):
     FETCH_SIZE, WRITE_SIZE and name in copy (python bench.py --calibrate-copy)
     and each workload (python bench.py --workload W --no-cpu-baseline).  Each
     counter is scaled by the factor that makes it read 1 GiB for the 1 GiB
-    copy; the GEMM dispatches of a workload cycle through its layers in order.
+    copy.  A GEMM call is the dispatch (or, for a K-split call, the full-K
+    dispatch, the split dispatch and the reduction) that directly follows an
+    activation quantization; those calls come from the warm-up and timed
+    steps, which cycle through the layers in order (the back-to-back GEMM
+    launches of the kernel timing are not counted).
     """
     import csv
 
@@ -223,6 +227,28 @@ def write_traffic(prof_dir, workloads):
         with open(path) as f:
             r = list(csv.DictReader(f))
         return sorted((int(x["Dispatch_Id"]), x["Kernel_Name"], float(x["Counter_Value"])) for x in r)
+
+    def is_quant(k):
+        return "quantize" in k
+
+    def is_gemm(k):
+        return ("gemm" in k or "split_reduce" in k) and not is_quant(k)
+
+    def step_calls(counter, name):
+        """Per GEMM call of the steps: (kernel names, summed counter), in order."""
+        d = rows(counter, name)
+        calls = []
+        for i in range(len(d) - 1):
+            if not (is_quant(d[i][1]) and is_gemm(d[i + 1][1])):
+                continue
+            n = 1
+            if i + 2 < len(d) and "split_reduce" in d[i + 2][1]:
+                n = 2
+            elif i + 3 < len(d) and "split_reduce" in d[i + 3][1] and is_gemm(d[i + 2][1]):
+                n = 3
+            part = d[i + 1:i + 1 + n]
+            calls.append(([k for _, k, _ in part], sum(v for _, _, v in part)))
+        return calls
 
     def copies(counter):
         v = [val for _, k, val in rows(counter, "copy") if "copyBuffer" in k]
@@ -239,10 +265,10 @@ def write_traffic(prof_dir, workloads):
            "calibration": cal, "workloads": {}}
     for wl in workloads:
         _, M, layers, ga, gw, _ = WORKLOADS[wl]
-        gemm = lambda c: [v for _, k, v in rows(c, wl) if "gemm" in k and "quantize" not in k]
-        names = {k for _, k, _ in rows("FETCH_SIZE", wl) if "gemm" in k and "quantize" not in k}
+        fc, wc = step_calls("FETCH_SIZE", wl), step_calls("WRITE_SIZE", wl)
+        names = {k for ks, _ in fc for k in ks}
         files = kernel_source_files(names)
-        fr, wr = gemm("FETCH_SIZE"), gemm("WRITE_SIZE")
+        fr, wr = [v for _, v in fc], [v for _, v in wc]
         per = []
         for li, (K, N) in enumerate(layers):
             f = fr[li::len(layers)]
