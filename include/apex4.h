@@ -89,9 +89,12 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
  * most half the GPU's compute units: those tiles then run as P = min(CUs /
  * tiles, K / 256, 4) parts of K into fp32 partial tiles in the workspace
  * (P x tiles x 256 x 128 x 4 bytes, e.g. 25.2 MB for M = 2048, N = 22016 on
- * 256 CUs) and a reduction adds the parts in a fixed order.  0 for invalid or
- * empty shapes.  The workspace holds nothing between calls; calls that
- * overlap on one workspace race.
+ * 256 CUs) and a reduction adds the parts in a fixed order.  Also nonzero
+ * for 17 <= M <= 64 rows (groups of 128 or mixed) when the 16-column blocks
+ * leave at most 2 per compute unit and K >= 4096: the kernel then walks two
+ * halves of K (2 x M x N x 4 bytes, e.g. 4 MB for M = 64, N = 8192).  0 for
+ * invalid or empty shapes.  The workspace holds nothing between calls; calls
+ * that overlap on one workspace race.
  */
 size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a,
                                  int32_t group_w);

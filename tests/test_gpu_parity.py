@@ -337,3 +337,17 @@ def test_gemm_split_workspace_too_small(dev):
                                      M, N, K, apex4._ptr(y), None, None, apex4._ptr(ws), need - 16,
                                      torch.cuda.current_stream().cuda_stream)
     assert st == 4   # APEX4_ERR_WORKSPACE, nothing launched
+
+
+@pytest.mark.parametrize("M", [17, 40, 64])
+@pytest.mark.parametrize("N,K", [(8192, 8192), (1000, 5248)])
+@pytest.mark.parametrize("ga,gw", [(128, 128), (128, "K")])
+def test_gemm_decode_split_k(dev, M, N, K, ga, gw):
+    """17-64 rows with at most 2 column blocks per workgroup (N = 8192: 512
+    blocks; N = 1000: 63): the K-outer kernel's two K halves (K = 5248: 6
+    items, the last ragged) into the workspace, then the reduction."""
+    gw = K if gw == "K" else gw
+    ws = apex4.workspace_size(M, N, K, ga, gw)
+    assert ws == 2 * M * N * 4
+    x, w = inputs.problem(M, N, K, seed=61 + M, act="outlier")
+    run_case(dev, x, w, ga, gw, rows=None if M <= 17 else sample_rows(M))

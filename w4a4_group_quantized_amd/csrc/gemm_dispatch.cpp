@@ -12,14 +12,14 @@ namespace apex4 {
 
 size_t gemm_workspace_bytes(const GemmProblem& p)
 {
-    // mirrors the order of launch_gemm: only the ping-pong kernel uses one
+    // mirrors the order of launch_gemm: the K-outer and ping-pong kernels' K splits
     if (p.M <= 2 && gemv_supports(p)) return 0;
 #ifndef APEX4_NO_STREAM
     if (stream_supports(p)) return 0;
 #endif
     if (gemv_supports(p)) return 0;
 #ifndef APEX4_NO_KOUTER
-    if (kouter_supports(p)) return 0;
+    if (kouter_supports(p)) return kouter_workspace_bytes(p);
 #endif
     if (skinny_supports(p)) return 0;
 #ifndef APEX4_NO_PINGPONG

@@ -26,6 +26,12 @@
 // cannot always tell the direct-to-LDS copies into different buffers apart and
 // would drain them.
 //
+// K split.  With at most 2 column blocks per workgroup (e.g. N = 8192: 512
+// blocks on 256 CUs) an item's activation rows serve only 2 blocks' weights.
+// Then (groups of 128) the workgroups form two sets, each walking half of K
+// over twice the blocks; their fp32 results go to the caller's workspace and
+// a small kernel adds the two halves in a fixed order.
+//
 // Each of the 8 waves owns 128 K values of every item, i.e. one group of 128:
 // two K-steps per row tile.  Its activation fragments and s_a for the item are
 // read from LDS once, at the item's first unit.  At the end of a group the
@@ -69,6 +75,12 @@ struct KouterArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    // K split (groups of 128): the workgroups come in kparts equal sets, set q
+    // walking items [q items / kparts, (q+1) items / kparts) of its blocks
+    // (dealt round-robin within the set) and writing its fp32 results to
+    // part[q] ([M][N]) for the reduction kernel; kparts = 1: no split.
+    int kparts;
+    float* part;
 };
 
 // LDS: NBUF unit buffers (16 weight-row pieces, then s_w in 8 regions of 64
@@ -193,9 +205,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t rowbytes = (uint32_t)a.K / 2;
-    const int nb = blockIdx.x < a.blocks ? (a.blocks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    // this workgroup's set (K part) and its index within the set
+    const int wgs = gridDim.x / a.kparts;
+    const int kq = blockIdx.x / wgs, wid = blockIdx.x - kq * wgs;
+    const int item0 = kq * a.items / a.kparts;
+    const int nit = (kq + 1) * a.items / a.kparts - item0;    // items walked
+    const int nb = wid < a.blocks ? (a.blocks - 1 - wid) / wgs + 1 : 0;
     const int ngroups = (nb + BG - 1) / BG;
-    const int n_items = ngroups * a.items;                 // (group, item) pairs
+    const int n_items = ngroups * nit;                     // (group, item) pairs
     const int total = n_items * BG;                        // units
     const __amdgpu_buffer_rsrc_t rW = buffer_of(a.qw, (uint32_t)a.N * rowbytes);
     const __amdgpu_buffer_rsrc_t rA = buffer_of(a.qa, (uint32_t)a.M * rowbytes);
@@ -205,14 +222,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
     const int m_out = 4 * fkb;                             // output rows m_out..m_out+3 of a row tile
     const int slot_k = (4 * wave + fkb) ^ fi;              // LDS slot of this lane's chunk of row fi
 
-    // unit u: group u / (items * BG), item (u / BG) % items, block slot u % BG
+    // unit u: group u / (nit * BG), item item0 + (u / BG) % nit, block slot u % BG
     auto unit_block = [&](int u, int& b, int& it, bool& live) {
         const int ii = u / BG, j = u - ii * BG;
-        const int grp = ii / a.items;
-        it = ii - grp * a.items;
+        const int grp = ii / nit;
+        it = item0 + ii - grp * nit;
         const int slot = grp * BG + j;
         live = u < total && slot < nb;
-        b = blockIdx.x + gridDim.x * slot;
+        b = wid + wgs * slot;
     };
 
     // --- copy of unit u into buffer bi: weight rows 2w (lanes 0-31) and
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
     // group w of the item's s_a (lane l: row l) ---
     auto load_item = [&](int ii) {
         const bool live = ii < n_items;
-        const int it = live ? ii % a.items : 0;
+        const int it = item0 + (live ? ii % nit : 0);
         uint8_t* d = lds_act[ii & 1];
 #pragma unroll
         for (int k = 0; k < MT; ++k) {
@@ -288,13 +305,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
     // of column l & 15, (tile, register) pairs 2w and 2w + 1 (MT = 4) or w
     // (MT = 2), in wave order, and stores them.
     auto finish_group = [&](int ii) {
-        const int grp = ii / a.items;
+        const int grp = ii / nit;
         float* red = reinterpret_cast<float*>(lds_act[ii & 1]);
         const float* sab = lds_sa[ii & 1];
 #pragma unroll
         for (int j = 0; j < BG; ++j) {
             const int slot = grp * BG + j;
-            const int b = blockIdx.x + gridDim.x * slot;
+            const int b = wid + wgs * slot;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const uint32_t p = lds_addr(&red[((wave * 64 + lane) * MT + mt) * 4]);
@@ -335,8 +352,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
                     asm volatile("" : "+v"(v));   // y16 is the fp16 rounding of y32
                     if (m < a.M && n < a.N) {
                         const int64_t off = (int64_t)m * a.N + n;
-                        a.y16[off] = (_Float16)v;
-                        if (a.y32) a.y32[off] = v;
+                        if (a.part) {
+                            a.part[(int64_t)kq * a.M * a.N + off] = v;
+                        } else {
+                            a.y16[off] = (_Float16)v;
+                            if (a.y32) a.y32[off] = v;
+                        }
                     }
                 }
             }
@@ -427,17 +448,43 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
                 }
             }
         }
-        if (j == BG - 1 && it == a.items - 1) finish_group(ii);
+        if (j == BG - 1 && it == item0 + nit - 1) finish_group(ii);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+}
+
+// Y = the K parts' results added in part order (fp16 the RNE rounding of the
+// fp32 sum); one thread per output
+__global__ __launch_bounds__(256) void kouter_split_reduce_kernel(KouterArgs a)
+{
+    const int64_t mn = (int64_t)a.M * a.N;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= mn) return;
+    float v = a.part[i];
+    for (int q = 1; q < a.kparts; ++q) v += a.part[q * mn + i];
+    asm volatile("" : "+v"(v));
+    a.y16[i] = (_Float16)v;
+    if (a.y32) a.y32[i] = v;
+}
+
+// workgroups: one per block up to 256, in kparts equal sets
+int kouter_grid(const KouterArgs& s)
+{
+    const int want = s.blocks * s.kparts;
+    const int g = want < 256 ? want : 256;
+    return g - g % s.kparts;
 }
 
 template <int GM, bool MIXED, int MT, int BG>
 hipError_t launch_g(const KouterArgs& s, bool dbg, hipStream_t stream)
 {
-    const int grid = s.blocks < 256 ? s.blocks : 256;
+    const int grid = kouter_grid(s);
     if (dbg) gemm_kouter_kernel<GM, MIXED, true, MT, BG><<<grid, THREADS, 0, stream>>>(s);
     else gemm_kouter_kernel<GM, MIXED, false, MT, BG><<<grid, THREADS, 0, stream>>>(s);
+    if (s.kparts > 1) {
+        const int64_t mn = (int64_t)s.M * s.N;
+        kouter_split_reduce_kernel<<<(unsigned)((mn + 255) / 256), 256, 0, stream>>>(s);
+    }
     return hipGetLastError();
 }
 
@@ -445,8 +492,8 @@ hipError_t launch_g(const KouterArgs& s, bool dbg, hipStream_t stream)
 template <int GM, bool MIXED, int MT>
 hipError_t launch_mt(const KouterArgs& s, bool dbg, hipStream_t stream)
 {
-    const int grid = s.blocks < 256 ? s.blocks : 256;
-    const int per_wg = (s.blocks + grid - 1) / grid;
+    const int wgs = kouter_grid(s) / s.kparts;
+    const int per_wg = (s.blocks + wgs - 1) / wgs;
     if (per_wg <= 2) return launch_g<GM, MIXED, MT, 2>(s, dbg, stream);
     if (per_wg <= 4 || MT == 4) return launch_g<GM, MIXED, MT, 4>(s, dbg, stream);
     return launch_g<GM, MIXED, MT, MT == 4 ? 4 : 8>(s, dbg, stream);
@@ -460,6 +507,26 @@ hipError_t launch_mode(const KouterArgs& s, bool dbg, hipStream_t stream)
 }
 
 }  // namespace
+
+int kouter_kparts(const GemmProblem& p)
+{
+    // Two K parts when a workgroup would get at most 2 column blocks (groups
+    // of 128 only, at least 2 items per part): each workgroup then walks half
+    // the items over twice the blocks, so each item's activation rows serve
+    // twice the weight bytes (and with fewer than 256 blocks, twice the CUs
+    // work).  One group over K keeps its single rounding.
+    const int gs = p.ga < p.gw ? p.ga : p.gw;
+    const int blocks = (p.N + ROWS - 1) / ROWS, items = (p.K + IK - 1) / IK;
+    const int grid = blocks < 256 ? blocks : 256;
+    if (gs != 128 || items < 4 || (blocks + grid - 1) / grid > 2) return 1;
+    return 2;
+}
+
+size_t kouter_workspace_bytes(const GemmProblem& p)
+{
+    const int kp = kouter_kparts(p);
+    return kp > 1 ? (size_t)kp * p.M * p.N * sizeof(float) : 0;
+}
 
 bool kouter_supports(const GemmProblem& p)
 {
@@ -497,6 +564,11 @@ hipError_t launch_gemm_kouter(const GemmProblem& p, hipStream_t stream)
     s.y16 = static_cast<_Float16*>(p.y16);
     s.y32 = p.y32;
     s.psum = p.psum;
+    s.kparts = kouter_kparts(p);
+    s.part = static_cast<float*>(p.ws);
+    // the split needs its workspace, and is not used for the debug sums
+    if (s.kparts > 1 && (p.psum || !p.ws || p.ws_bytes < kouter_workspace_bytes(p))) s.kparts = 1;
+    if (s.kparts == 1) s.part = nullptr;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     const bool dbg = p.psum != nullptr;
     if (mixed) return launch_mode<1, true>(s, dbg, stream);

@@ -37,6 +37,10 @@ struct PingpongSplit {
 };
 PingpongSplit pingpong_split(const GemmProblem& p);
 
+// The K-outer kernel's K split (2 parts, or 1: none) and its fp32 workspace.
+int kouter_kparts(const GemmProblem& p);
+size_t kouter_workspace_bytes(const GemmProblem& p);
+
 // Device workspace the call needs (0 for most shapes): the kernel choice of
 // launch_gemm, shapes only.
 size_t gemm_workspace_bytes(const GemmProblem& p);
