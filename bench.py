@@ -58,6 +58,9 @@ WORKLOADS = {
     "sweep-mixed": ("granularity sweep, mixed (per-channel weights, g=128 activations)", 8192,
                     [(8192, 28672)], 128, 8192, "student_t"),
 }
+# The same layer sets on FP8-coded operands (apex4_quantize_f8, apex4_gemm_w4a4_f8):
+# name -> the INT4 workload it mirrors
+F8_WORKLOADS = {"llama2-7b-prefill-f8": "llama2-7b-prefill", "llama2-70b-prefill-f8": "llama2-70b-prefill"}
 # Whole-layer workloads (w4a4_group_quantized_amd/linear.py, LlamaLayerW4A4):
 # name -> (description, M, hidden, intermediate)
 LAYER_WORKLOADS = {
@@ -77,7 +80,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama2-7b-prefill", choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS))
+    ap.add_argument("--workload", default="llama2-7b-prefill",
+                    choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS) + sorted(F8_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the GPU's measured ceilings")
@@ -343,9 +347,24 @@ def main():
     import torch
     from w4a4_group_quantized_amd import apex4
 
-    desc, M, layers, ga, gw, act = WORKLOADS[args.workload]
+    f8 = args.workload in F8_WORKLOADS
+    desc, M, layers, ga, gw, act = WORKLOADS[F8_WORKLOADS.get(args.workload, args.workload)]
+    if f8:
+        desc += ", FP8-coded operands (one E4M3 byte per INT4 code)"
     dev = torch.device("cuda:0")
     apex4.lib()
+
+    # the path's three calls: activation quantization, weight packing, GEMM
+    if f8:
+        quant = lambda tx, out: apex4.quantize_f8(tx, ga, out=out)
+        pack = lambda tw: apex4.quantize_f8(tw, gw)
+        gemm = lambda qa, sa, qw, sw, K, y: apex4.gemm_f8(qa, sa, qw, sw, y16=y)
+        code_cols = lambda K: K
+    else:
+        quant = lambda tx, out: apex4.quantize_act(tx, ga, out=out)
+        pack = lambda tw: apex4.pack_weight(tw, gw)
+        gemm = lambda qa, sa, qw, sw, K, y: apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
+        code_cols = lambda K: K // 2
 
     # --- resident inputs: fp16 activations per layer, weights packed once.
     # Memory-bound workloads cycle through enough independent copies (>= 1 GiB
@@ -360,8 +379,8 @@ def main():
         for (K, N) in layers:
             x, w = inputs.problem(M, N, K, seed=c, act=act)
             tx = torch.from_numpy(x).to(dev)
-            qw, sw = apex4.pack_weight(torch.from_numpy(w).to(dev), gw)
-            qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            qw, sw = pack(torch.from_numpy(w).to(dev))
+            qa = torch.empty((M, code_cols(K)), dtype=torch.uint8, device=dev)
             sa = torch.empty((M, K // ga), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             data.append((K, N, tx, qa, sa, qw, sw, y))
@@ -369,12 +388,13 @@ def main():
     torch.cuda.synchronize()
 
     ops_step = sum(rl.gemm_ops(M, N, K) for (K, N) in layers)
-    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) for (K, N) in layers]
+    # (FP8-coded operands: one byte per code instead of half)
+    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0) for (K, N) in layers]
 
     def step(i):
         for (K, N, tx, qa, sa, qw, sw, y) in sets[i % copies]:
-            apex4.quantize_act(tx, ga, out=(qa, sa))
-            apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
+            quant(tx, (qa, sa))
+            gemm(qa, sa, qw, sw, K, y)
 
     for i in range(args.warmup):
         step(i)
@@ -421,7 +441,7 @@ def main():
         def gemms():
             for r in range(R):
                 (_, _, _, qa, sa, qw, sw, y) = sets[r % copies][li]
-                apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
+                gemm(qa, sa, qw, sw, K, y)
         if graphs is not None:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
@@ -476,7 +496,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on i8 MFMA (i32 sums), f32 rescale",
+        "dtype": ("int4 codes as e4m3 bytes on the fp8 MFMA (exact f32 sums), f32 rescale" if f8 else
+                  "int4 codes on i8 MFMA (i32 sums), f32 rescale"),
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "layers_KN": layers, "group_a": ga, "group_w": gw,
                    "activations": act, "timed": "quantize_act + gemm per layer",
@@ -486,7 +507,7 @@ def main():
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
-                     "kernel": "gemm (apex4_gemm_w4a4)",
+                     "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else "gemm (apex4_gemm_w4a4)",
                      "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3),
                      "measured_ceiling": measured,
                      "frac_of_measured": None if measured is None else achieved / measured},

@@ -91,7 +91,7 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
  * (P x tiles x 256 x 128 x 4 bytes, e.g. 25.2 MB for M = 2048, N = 22016 on
  * 256 CUs) and a reduction adds the parts in a fixed order.  Also nonzero
  * for 17 <= M <= 64 rows (groups of 128 or mixed) when the 16-column blocks
- * leave at most 2 per compute unit and K >= 4096: the kernel then walks two
+ * leave at most 2 per compute unit and K > 3072: the kernel then walks two
  * halves of K (2 x M x N x 4 bytes, e.g. 4 MB for M = 64, N = 8192).  0 for
  * invalid or empty shapes.  The workspace holds nothing between calls; calls
  * that overlap on one workspace race.
@@ -127,6 +127,42 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
                              int64_t M, int64_t N, int64_t K,
                              void* y_f16, float* y_f32, int32_t* psum_dbg,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8-coded operands: a variant of the same GEMM whose operands hold one byte
+ * per code instead of two nibbles.  The INT4 codes -8..7 are exact values of
+ * FP8 E4M3 (the OCP format of gfx950), and gfx950's FP8 matrix instruction
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales) sums their exact
+ * products in fp32, which for these integers is exact (|group sum| <= 64 *
+ * 128 < 2^24): the per-group sums P_j and the result are those of
+ * apex4_gemm_w4a4, while the int32 -> fp32 conversion of the rescale and the
+ * nibble widening go away.  The price is twice the operand bytes.  (The OSC
+ * page, Abstract, points to 4-bit micro-scaling matrix hardware as the way
+ * ahead; the APEX4 page's own kernels run on INT4 tensor cores.)
+ *
+ * apex4_quantize_f8: the quantization rule of apex4_quantize_act /
+ * apex4_pack_weight (groups of 128), codes written as E4M3 bytes, one per
+ * element in K order (-0 is written as +0).
+ *   x_f16 [rows, K] fp16, 16-byte aligned; rows >= 0 (0: no-op), K % 128 == 0.
+ *   q8 [rows, K] bytes, 8-byte aligned;  s [rows, K/128] fp32, as apex4_quantize_act.
+ *   group: 128 only (other valid groups: APEX4_ERR_UNSUPPORTED).
+ */
+apex4_status apex4_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q8,
+                               float* s, void* stream);
+
+/*
+ * apex4_gemm_w4a4_f8: Y of apex4_gemm_w4a4 with group_a = group_w = 128 from
+ * E4M3-coded operands (apex4_quantize_f8 outputs).
+ *   qa8 [M, K], qw8 [N, K] bytes, 16-byte aligned; s_a [M, K/128], s_w [N, K/128].
+ *   y_f16 [M, N], y_f32 [M, N] or NULL, psum_dbg [M, N, K/128] int32 or NULL,
+ *   as in apex4_gemm_w4a4 (the fp32 summation order is not fixed; P exact).
+ *   M, N >= 0 (0: no-op), K > 0, K % 128 == 0, 256 * K < 2^31.  Any M works;
+ *   the kernel is the compute-bound one (256 x 128 output tiles), meant for
+ *   prefill-sized M.  No workspace.  Asynchronous on `stream`.
+ */
+apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* qw8, const float* s_w,
+                                int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                int32_t* psum_dbg, void* stream);
 
 /*
  * Granularity selection for a GEMM shape on this GPU (APEX4 page, Abstract:

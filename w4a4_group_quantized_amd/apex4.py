@@ -30,6 +30,8 @@ SIGNATURES = {
     "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "apex4_gemm_w4a4_f8": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
                                         ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
@@ -143,6 +145,46 @@ def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bo
     _check("apex4_gemm_w4a4", lib().apex4_gemm_w4a4(
         _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K,
         _ptr(y16), _ptr(y32), _ptr(psum), _ptr(ws), ws_bytes, _stream(torch, dev)))
+    if want_y32 or want_psum:
+        return y16, y32, psum
+    return y16
+
+
+def quantize_f8(x, group: int = 128, out=None):
+    """x: fp16 [rows, K] GPU tensor -> (q8 uint8 [rows, K] E4M3 codes, s float32 [rows, K/group])
+    (apex4_quantize_f8: the rule of quantize_act / pack_weight, one byte per code)."""
+    import torch
+    _need_gpu(x, "x", torch.float16)
+    rows, K = x.shape
+    if out is None:
+        q8 = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, K // group if group > 0 else 0), dtype=torch.float32, device=x.device)
+    else:
+        q8, s = out
+    _check("apex4_quantize_f8", lib().apex4_quantize_f8(
+        _ptr(x), rows, K, group, _ptr(q8), _ptr(s), _stream(torch, x.device)))
+    return q8, s
+
+
+def gemm_f8(qa8, sa, qw8, sw, *, want_y32: bool = False, want_psum: bool = False, y16=None, y32=None):
+    """apex4_gemm_w4a4_f8: the W4A4 GEMM (groups of 128) on E4M3-coded operands.
+    Returns y16, or (y16, y32, psum) when want_y32/want_psum is set."""
+    import torch
+    for t, n in ((qa8, "qa8"), (qw8, "qw8")):
+        _need_gpu(t, n, torch.uint8)
+    for t, n in ((sa, "s_a"), (sw, "s_w")):
+        _need_gpu(t, n, torch.float32)
+    M, K = qa8.shape
+    N = qw8.shape[0]
+    dev = qa8.device
+    if y16 is None:
+        y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if want_y32 and y32 is None:
+        y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    psum = torch.empty((M, N, K // 128), dtype=torch.int32, device=dev) if want_psum else None
+    _check("apex4_gemm_w4a4_f8", lib().apex4_gemm_w4a4_f8(
+        _ptr(qa8), _ptr(sa), _ptr(qw8), _ptr(sw), M, N, K, _ptr(y16), _ptr(y32), _ptr(psum),
+        _stream(torch, dev)))
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16

@@ -65,6 +65,46 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
                                             static_cast<hipStream_t>(stream)));
 }
 
+apex4_status apex4_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q8,
+                               float* s, void* stream)
+{
+    if (group != 128) return group > 0 && K > 0 && K % group == 0 ? APEX4_ERR_UNSUPPORTED : APEX4_ERR_INVALID_ARG;
+    const apex4_status st = check_quantize(x_f16, rows, K, group, q8, s);
+    if (st != APEX4_OK || rows == 0) return st;
+    if (!aligned(q8, 8)) return APEX4_ERR_ALIGNMENT;
+    return to_status(apex4::launch_quantize_f8(x_f16, rows, K, q8, s, static_cast<hipStream_t>(stream)));
+}
+
+apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* qw8, const float* s_w,
+                                int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32, int32_t* psum_dbg,
+                                void* stream)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (psum_dbg && M * N * (K / 128) > kMaxDim) return APEX4_ERR_INVALID_ARG;
+    // 32-bit offsets within a 256-row block of operand bytes
+    if ((uint64_t)K * 256 >= (1ull << 31)) return APEX4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return APEX4_OK;
+    if (!qa8 || !s_a || !qw8 || !s_w || !y_f16) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(qa8, 16) || !aligned(qw8, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(y_f16, 2) ||
+        !aligned(y_f32, 4) || !aligned(psum_dbg, 4))
+        return APEX4_ERR_ALIGNMENT;
+    apex4::GemmProblem p{};
+    p.qa = static_cast<const uint8_t*>(qa8);
+    p.sa = s_a;
+    p.qw = static_cast<const uint8_t*>(qw8);
+    p.sw = s_w;
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.ga = 128;
+    p.gw = 128;
+    p.y16 = y_f16;
+    p.y32 = y_f32;
+    p.psum = psum_dbg;
+    return to_status(apex4::launch_gemm_pingpong_f8(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w)
 {
     // shapes apex4_gemm_w4a4 rejects, or that launch nothing, need none

@@ -43,6 +43,12 @@
 // offset would only leave each SIMD's matrix unit with one wave).  Mixed mode (per-channel weight scales, activation groups
 // of 128) rescales with s_a alone and applies s_w in the epilogue.
 //
+// FP8-coded operands (apex4_gemm_w4a4_f8).  The same kernel with each code
+// stored as its exact E4M3 byte: the copy stores the bytes as they come (no
+// widening), a 128-code stage is two K-steps of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), whose fp32 result is
+// the exact group sum, so the rescale is one fma per output; no 2^-8 fold.
+//
 // Rounds of tiles.  One workgroup fills a CU, so a launch runs in rounds of
 // one tile per CU.  A last round that would leave more than half the CUs
 // idle (e.g. 96 of 256, or a call with only a few tiles) is run as 2 to 4
@@ -52,10 +58,13 @@
 // as the epilogue does.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace apex4 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -171,9 +180,18 @@ __device__ inline void lds_barrier()
 
 // SPG: stages per group, 1 (g = 128), 2 (g = 256) or 0 (one group, g = K).
 // EARLY: this wave belongs to waves 0..3.
-template <bool MIXED, bool DEBUG_P, int SPG, bool EARLY>
+// F8: FP8-coded operands (one byte per code, the codes' exact E4M3 values):
+// a stage of 128 codes is 128 bytes per row, copied in 6 chunks per thread
+// through one register set (stored before the next stage's loads are
+// issued), two 64-code K-steps of the FP8 MFMA.
+template <bool MIXED, bool DEBUG_P, int SPG, bool EARLY, bool F8>
 __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
 {
+    constexpr int KST = KSTAGE;                  // K values per stage
+    constexpr int ROWB_S = F8 ? 128 : ROWB;      // operand bytes per row per stage
+    constexpr int CPR = ROWB_S / 16;             // 16-byte chunks per row per stage
+    constexpr int NCH = 3 * CPR / 4;             // chunks per thread per stage
+    constexpr int NSET = F8 ? 1 : 2;             // register sets of the copy
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,9 +204,9 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const int tile = a.tile0 + lin;
     const int by = tile / a.tiles_n, bx = tile - by * a.tiles_n;
     const int m0 = by * BM, n0 = bx * BN;
-    const uint32_t rowbytes = (uint32_t)a.K / 2;
+    const uint32_t rowbytes = F8 ? (uint32_t)a.K : (uint32_t)a.K / 2;
     // this workgroup's stages: s0 .. s0 + stages - 1
-    const int all_stages = a.K / KSTAGE;
+    const int all_stages = a.K / KST;
     const int s0 = a.part ? kpart * all_stages / a.nparts : 0;
     const int stages = a.part ? (kpart + 1) * all_stages / a.nparts - s0 : all_stages;
     const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
@@ -199,34 +217,35 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const __amdgpu_buffer_rsrc_t rSA = buffer_of(a.sa + (int64_t)m0 * a.Ga, (uint32_t)rows_a * a.Ga * 4);
     const __amdgpu_buffer_rsrc_t rSW = buffer_of(a.sw + (int64_t)n0 * a.Gw, (uint32_t)rows_b * a.Gw * 4);
 
-    // --- this thread's share of a stage copy: 3 chunks of 16 packed bytes
-    // (one 32-code K-step of a row).  Waves 0..3: A rows 0..191 and the A
-    // scales; waves 4..7: A rows 192..255, all of B and the B scales. ---
+    // --- this thread's share of a stage copy: NCH chunks of 16 bytes (3 of
+    // packed codes, one 32-code K-step of a row each; FP8: 6 of 16 codes).
+    // Waves 0..3: A rows 0..191 and the A scales; waves 4..7: A rows
+    // 192..255, all of B and the B scales. ---
     const int ht = EARLY ? tid : tid - HALF;
-    uint32_t goff[3], loff[3];
+    uint32_t goff[NCH], loff[NCH];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         int c;
-        if (EARLY) c = ht + HALF * j;                      // A chunks 0..767
-        else c = j == 0 ? 3 * HALF + ht : ht + HALF * (j - 1);   // A 768..1023; B 0..511
-        const int row = c >> 2, s = c & 3;
+        if (EARLY) c = ht + HALF * j;                                  // A rows 0..191
+        else c = j < CPR / 4 ? 192 * CPR + ht + HALF * j : ht + HALF * (j - CPR / 4);   // A 192..255; B
+        const int row = (unsigned)c / CPR, s = (unsigned)c % CPR;
         goff[j] = (uint32_t)row * rowbytes + 16 * s;
-        loff[j] = row * STRIDE + 32 * s;
+        loff[j] = row * STRIDE + (F8 ? 16 : 32) * s;
     }
-    // chunk j's operand: A, or B for chunks 1 and 2 of waves 4..7
-    auto chunk_is_b = [](int j) { return !EARLY && j > 0; };
+    // chunk j's operand: A, or B for the chunks past the first CPR/4 of waves 4..7
+    auto chunk_is_b = [](int j) { return !EARLY && j >= CPR / 4; };
     const bool has_scale = EARLY ? true : (!MIXED && ht < BN);
     // threads without a scale row load from past the end (zeros), so that
     // every load is unconditional and the wait counts stay exact
     const uint32_t soff = !has_scale ? 0x80000000u : EARLY ? (uint32_t)ht * a.Ga * 4 : (uint32_t)ht * a.Gw * 4;
 
-    uint4 rq[2][3];
-    float rs[2];
+    uint4 rq[NSET][NCH];
+    float rs[NSET];
     auto load_stage = [&](int t, int set) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             const u32x4 v =
-                __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], (s0 + t) * ROWB, 0);
+                __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], (s0 + t) * ROWB_S, 0);
             rq[set][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
         // the scale of the group that stage t belongs to
@@ -236,16 +255,21 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     };
     auto store_stage = [&](int buf, int set) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) anchor(rq[set][j]);   // widen in this phase
+        for (int j = 0; j < NCH; ++j) anchor(rq[set][j]);   // widen in this phase
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             uint8_t* base = chunk_is_b(j) ? sh.b[buf] : sh.a[buf];
-            *reinterpret_cast<uint4*>(base + loff[j]) = widen_lo(rq[set][j]);
-            *reinterpret_cast<uint4*>(base + loff[j] + 16) = widen_hi(rq[set][j]);
+            if (F8) {
+                *reinterpret_cast<uint4*>(base + loff[j]) = rq[set][j];
+            } else {
+                *reinterpret_cast<uint4*>(base + loff[j]) = widen_lo(rq[set][j]);
+                *reinterpret_cast<uint4*>(base + loff[j] + 16) = widen_hi(rq[set][j]);
+            }
         }
         if (EARLY) {
-            // A scale of row ht, with the 2^-8 of the widened operands folded in
-            const float s = rs[set] * 0.00390625f;
+            // A scale of row ht, with the 2^-8 of the widened operands folded
+            // in (FP8 codes are the values themselves)
+            const float s = F8 ? rs[set] : rs[set] * 0.00390625f;
             if (MIXED) {
                 reinterpret_cast<float*>(sh.ta[buf])[ht] = s;
             } else {
@@ -268,17 +292,20 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
-    v16i P[2][2];
+    using PT = typename std::conditional<F8, v16f, v16i>::type;
+    PT P[2][2];
     v16f S[2][2];   // scale products of the group in P
     if (SPG == 0) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) P[mt][nt] = v16i{};
+            for (int nt = 0; nt < 2; ++nt) P[mt][nt] = PT{};
     }
 
-    const uint32_t frag = (wm * 64 + (lane & 31)) * STRIDE + 16 * (lane >> 5);
-    const uint32_t fragb = (wn * 64 + (lane & 31)) * STRIDE + 16 * (lane >> 5);
+    // fragment bases: row lane & 31 of the wave's tiles, K bytes from 16 (or,
+    // FP8, 32) * (lane >> 5)
+    const uint32_t frag = (wm * 64 + (lane & 31)) * STRIDE + (F8 ? 32 : 16) * (lane >> 5);
+    const uint32_t fragb = (wn * 64 + (lane & 31)) * STRIDE + (F8 ? 32 : 16) * (lane >> 5);
     const int trow = lane & 31, thalf = lane >> 5;
     // The scale products S of the 4 tiles for the group of stage buffer `buf`,
     // on the matrix unit, so that the vector phase has no LDS or matrix-unit
@@ -321,6 +348,32 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     auto mma_stage = [&](int buf, bool zero, bool ends) {
         const uint8_t* la = sh.a[buf] + frag;
         const uint8_t* lb = sh.b[buf] + fragb;
+        if constexpr (F8) {
+            // two K-steps of 64: 32 bytes per lane and tile each, 8 MFMAs
+            // (the stage is one group: P starts from zero)
+            v8i ga[2][2], gb[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const v4i a0 = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 64 * ks);
+                    const v4i a1 = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 64 * ks + 16);
+                    const v4i b0 = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 64 * ks);
+                    const v4i b1 = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 64 * ks + 16);
+                    ga[i][ks] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    gb[i][ks] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        P[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            ga[mt][ks], gb[nt][ks], ks == 0 ? v16f{} : P[mt][nt], 0, 0, 0, 127, 0, 127);
+            if (ends) scale_products(buf);
+            return;
+        }
         v4i fa[2][4], fb[2][4];
         // one group over K: P is live across stages but nothing else is, so
         // the fragments can all be read first as well
@@ -369,7 +422,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    int x = P[mt][nt][r];
+                    auto x = P[mt][nt][r];
                     anchor(x);
                     P[mt][nt][r] = x;
                     float y = S[mt][nt][r];
@@ -388,7 +441,8 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
-                        if (m < a.M && n < a.N) a.psum[((int64_t)m * a.N + n) * a.G + j] = P[mt][nt][r] >> 8;
+                        if (m < a.M && n < a.N)
+                            a.psum[((int64_t)m * a.N + n) * a.G + j] = F8 ? (int)P[mt][nt][r] : (int)P[mt][nt][r] >> 8;
                     }
                 }
             }
@@ -408,9 +462,15 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             else sh.tb[(i - 2 * BM) / BN][1][(i - 2 * BM) % BN] = make_uint4(0, 0, 0, 0);
         }
     }
-    load_stage(0, 0);
-    load_stage(1, 1);
-    store_stage(0, 0);
+    if constexpr (F8) {
+        load_stage(0, 0);
+        store_stage(0, 0);
+        load_stage(1, 0);
+    } else {
+        load_stage(0, 0);
+        load_stage(1, 1);
+        store_stage(0, 0);
+    }
     lds_barrier();
 
     // Stage t uses A/B and scale buffer t&1 and register set t&1; the loop is
@@ -429,6 +489,26 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         // end of K read other rows or zeros, and the stores go to a buffer
         // that is no longer read; unconditional memory operations keep the
         // wait counts exact (the loads of stage t+2 stay in flight).
+        if constexpr (F8) {
+            // FP8 operands, groups of one stage: the ping-pong as below with
+            // the copy's single register set stored (stage t+1) before the
+            // loads of stage t+2 are issued into it
+            if (EARLY) {
+                store_stage(h ^ 1, 0);
+                load_stage(t + 2, 0);
+                mma_stage(h, true, true);
+                lds_barrier();
+                rescale(t);
+                lds_barrier();
+            } else {
+                if (t > 0) rescale(t - 1);
+                lds_barrier();
+                store_stage(h ^ 1, 0);
+                load_stage(t + 2, 0);
+                mma_stage(h, true, true);
+                lds_barrier();
+            }
+        } else {
         if (SPG == 0) {
             // One group over K: no per-stage rescale to overlap, so both wave
             // groups run the matrix work of every stage at the same time (two
@@ -469,6 +549,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 store_stage(h ^ 1, h ^ 1);
             }
             lds_barrier();
+        }
         }
     }
     if (SPG == 0) {
@@ -519,15 +600,15 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         }
 }
 
-template <bool MIXED, bool DEBUG_P, int SPG>
+template <bool MIXED, bool DEBUG_P, int SPG, bool F8 = false>
 __global__ __launch_bounds__(THREADS, 2) void gemm_pp_kernel(PPArgs a)
 {
     __shared__ PPShared sh;
     // wave-uniform role (a scalar branch)
     if (__builtin_amdgcn_readfirstlane(threadIdx.x) < THREADS / 2)
-        pp_body<MIXED, DEBUG_P, SPG, true>(a, sh);
+        pp_body<MIXED, DEBUG_P, SPG, true, F8>(a, sh);
     else
-        pp_body<MIXED, DEBUG_P, SPG, false>(a, sh);
+        pp_body<MIXED, DEBUG_P, SPG, false, F8>(a, sh);
 }
 
 // Y of the K-split tiles: the parts' sums added in part order, then as the
@@ -650,6 +731,33 @@ bool pingpong_supports(const GemmProblem& p)
     // 32-bit buffer offsets within one workgroup's rows
     const uint64_t rowbytes = (uint64_t)p.K / 2;
     return rowbytes * BM < (1ull << 31) && (uint64_t)p.K / gs * 4 * BM < (1ull << 31);
+}
+
+hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
+{
+    // FP8-coded operands (qa, qw: [rows, K] bytes), groups of 128 on both
+    // operands (one stage per group)
+    PPArgs t{};
+    t.qa = p.qa;
+    t.sa = p.sa;
+    t.qw = p.qw;
+    t.sw = p.sw;
+    t.M = p.M;
+    t.N = p.N;
+    t.K = p.K;
+    t.Ga = p.K / 128;
+    t.Gw = p.K / 128;
+    t.spg = 1;
+    t.G = p.K / 128;
+    t.y16 = static_cast<_Float16*>(p.y16);
+    t.y32 = p.y32;
+    t.psum = p.psum;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.nparts = 1;
+    const int tiles = ((p.M + BM - 1) / BM) * t.tiles_n;
+    if (t.psum) gemm_pp_kernel<false, true, 1, true><<<tiles, THREADS, 0, stream>>>(t);
+    else gemm_pp_kernel<false, false, 1, true><<<tiles, THREADS, 0, stream>>>(t);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)

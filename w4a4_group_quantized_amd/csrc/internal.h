@@ -55,6 +55,10 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
 bool pingpong_supports(const GemmProblem& p);
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
+// FP8-coded operands (apex4_gemm_w4a4_f8): qa, qw hold one E4M3 byte per code
+hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* q8, float* s,
+                              hipStream_t stream);
 bool gemv_supports(const GemmProblem& p);
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);
 bool stream_supports(const GemmProblem& p);

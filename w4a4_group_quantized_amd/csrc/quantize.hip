@@ -2,7 +2,8 @@
 // offline): the rule of the APEX4 page's pure W4A4 scheme, with the readings
 // spelled out in include/apex4.h.  Memory-bound: 16-byte fp16 loads, one
 // packed 32-bit word (8 codes) per thread, group absmax by cross-lane
-// butterflies.  The scale and every quotient are IEEE fp32 divisions (the
+// butterflies (or the codes as FP8 bytes, for the FP8-operand GEMM).  The
+// scale and every quotient are IEEE fp32 divisions (the
 // library is built with correctly rounded fp32 division) and the rounding is
 // v_rndne_f32, so the codes are bit-identical to the rule.
 #include "internal.h"
@@ -55,6 +56,25 @@ __device__ inline uint32_t quantize8(const half8& h, float scale, bool nonzero)
     return word;
 }
 
+// The same 8 codes as FP8 E4M3 values, one byte each in K order (the codes
+// -8..7 are exact in E4M3; -0 is stored as +0).
+__device__ inline uint2 quantize8_f8(const half8& h, float scale, bool nonzero)
+{
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = 0.0f;
+    if (nonzero) {
+        const uint32_t word = quantize8(h, scale, true);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = (float)((int)(word << (28 - 4 * i)) >> 28) + 0.0f;
+    }
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+    return make_uint2(lo, hi);
+}
+
 // max over aligned groups of N lanes (N = 4, 8, 16, 32) with DPP lane moves
 // (no LDS round trip): quad swaps, then half-row and row mirrors; 32 lanes add
 // one cross-row exchange
@@ -75,11 +95,12 @@ __device__ inline float group_max(float v)
     return v;
 }
 
-// Group sizes 32..256: a group is G/8 consecutive lanes of one wave.
-template <int G>
+// Group sizes 32..256: a group is G/8 consecutive lanes of one wave.  F8:
+// the codes as FP8 bytes ([rows, K]) instead of packed nibbles.
+template <int G, bool F8>
 __global__ __launch_bounds__(256) void quantize_groups_kernel(const half8* __restrict__ x,
                                                               int64_t n8,
-                                                              uint32_t* __restrict__ q,
+                                                              void* __restrict__ q,
                                                               float* __restrict__ s)
 {
     constexpr int TPG = G / 8;
@@ -90,9 +111,9 @@ __global__ __launch_bounds__(256) void quantize_groups_kernel(const half8* __res
     const float amax = group_max<TPG>(absmax8(h));
     const float scale = amax / 7.0f;
     const bool nz = amax != 0.0f;
-    const uint32_t word = quantize8(h, scale, nz);
     if (live) {
-        q[t] = word;
+        if (F8) static_cast<uint2*>(q)[t] = quantize8_f8(h, scale, nz);
+        else static_cast<uint32_t*>(q)[t] = quantize8(h, scale, nz);
         if ((t % TPG) == 0) s[t / TPG] = nz ? scale : 0.0f;
     }
 }
@@ -130,14 +151,23 @@ hipError_t launch_quantize(const void* x_f16, int64_t rows, int64_t K, int32_t g
     const int64_t n8 = rows * (K / 8);
     const unsigned blocks = (unsigned)((n8 + 255) / 256);
     switch (g) {
-    case 32: quantize_groups_kernel<32><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
-    case 64: quantize_groups_kernel<64><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
-    case 128: quantize_groups_kernel<128><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
-    case 256: quantize_groups_kernel<256><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 32: quantize_groups_kernel<32, false><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 64: quantize_groups_kernel<64, false><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 128: quantize_groups_kernel<128, false><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
+    case 256: quantize_groups_kernel<256, false><<<blocks, 256, 0, stream>>>(x, n8, q, s); break;
     default:  // g == K, checked by the caller
         quantize_rows_kernel<<<(unsigned)rows, 256, 0, stream>>>(x, K / 8, q, s);
         break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* q8, float* s,
+                              hipStream_t stream)
+{
+    const int64_t n8 = rows * (K / 8);
+    const unsigned blocks = (unsigned)((n8 + 255) / 256);
+    quantize_groups_kernel<128, true><<<blocks, 256, 0, stream>>>(static_cast<const half8*>(x_f16), n8, q8, s);
     return hipGetLastError();
 }
 
