@@ -18,7 +18,8 @@
  *   - Pointers are DEVICE pointers (HIP device memory on the current device)
  *     unless a comment says otherwise.  Every tensor is row-major and
  *     contiguous.  The caller owns every buffer; the library allocates nothing,
- *     frees nothing and keeps no state between calls, so calls are re-entrant.
+ *     frees nothing and keeps no state between calls (beyond a host-side cache
+ *     of each device's compute-unit count), so calls are re-entrant.
  *   - Packed INT4 tensors hold two's-complement 4-bit codes, two per byte, code
  *     k of a row in byte k/2, the even k in the low nibble.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are

@@ -320,6 +320,13 @@ def test_gemm_split_last_round(dev, M, N, K, ga, gw):
         assert ws == 0
     rows = np.unique(np.concatenate([sample_rows(M, n=8), np.arange(M - 3, M), np.arange(256, min(M, 259))]))
     run_case(dev, x, w, ga, gw, rows=rows)
+    # the parts are added in a fixed order: a second call gives the same bits
+    tqa, tsa = gpu_quantize(x, ga, dev)
+    tqw, tsw = gpu_quantize(w, gw, dev, weight=True)
+    a = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True)[1]
+    b = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
 def test_gemm_split_workspace_too_small(dev):
@@ -351,3 +358,10 @@ def test_gemm_decode_split_k(dev, M, N, K, ga, gw):
     assert ws == 2 * M * N * 4
     x, w = inputs.problem(M, N, K, seed=61 + M, act="outlier")
     run_case(dev, x, w, ga, gw, rows=None if M <= 17 else sample_rows(M))
+    # the two halves are added in a fixed order: a second call gives the same bits
+    tqa, tsa = gpu_quantize(x, ga, dev)
+    tqw, tsw = gpu_quantize(w, gw, dev, weight=True)
+    a = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True)[1]
+    b = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

@@ -58,6 +58,7 @@
 // as the epilogue does.
 #include "internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace apex4 {
@@ -678,16 +679,17 @@ void launch_pp_all(const PPArgs& t, const PingpongSplit& sp, hipStream_t stream)
 
 int cu_count()
 {
-    // compute units of the current device (cached per device)
-    static int cached[64] = {};
+    // compute units of the current device, cached per device (relaxed atomics:
+    // concurrent first calls store the same value)
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 }  // namespace
