@@ -454,17 +454,40 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
 }
 
 // Y = the K parts' results added in part order (fp16 the RNE rounding of the
-// fp32 sum); one thread per output
+// fp32 sum); 4 consecutive outputs per thread, read as 16-byte vectors when
+// M*N is a multiple of 4 (then every part starts 16-byte aligned)
 __global__ __launch_bounds__(256) void kouter_split_reduce_kernel(KouterArgs a)
 {
     const int64_t mn = (int64_t)a.M * a.N;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= mn) return;
-    float v = a.part[i];
-    for (int q = 1; q < a.kparts; ++q) v += a.part[q * mn + i];
-    asm volatile("" : "+v"(v));
-    a.y16[i] = (_Float16)v;
-    if (a.y32) a.y32[i] = v;
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i0 >= mn) return;
+    float v[4];
+    if ((mn & 3) == 0) {
+        float4 p = *reinterpret_cast<const float4*>(a.part + i0);
+        v[0] = p.x, v[1] = p.y, v[2] = p.z, v[3] = p.w;
+        for (int q = 1; q < a.kparts; ++q) {
+            p = *reinterpret_cast<const float4*>(a.part + q * mn + i0);
+            v[0] += p.x, v[1] += p.y, v[2] += p.z, v[3] += p.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = 0.0f;
+            if (i0 + e < mn) {
+                v[e] = a.part[i0 + e];
+                for (int q = 1; q < a.kparts; ++q) v[e] += a.part[q * mn + i0 + e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (i0 + e < mn) {
+            float x = v[e];
+            asm volatile("" : "+v"(x));
+            a.y16[i0 + e] = (_Float16)x;
+            if (a.y32) a.y32[i0 + e] = x;
+        }
+    }
 }
 
 // workgroups: one per block up to 256, in kparts equal sets
@@ -483,7 +506,7 @@ hipError_t launch_g(const KouterArgs& s, bool dbg, hipStream_t stream)
     else gemm_kouter_kernel<GM, MIXED, false, MT, BG><<<grid, THREADS, 0, stream>>>(s);
     if (s.kparts > 1) {
         const int64_t mn = (int64_t)s.M * s.N;
-        kouter_split_reduce_kernel<<<(unsigned)((mn + 255) / 256), 256, 0, stream>>>(s);
+        kouter_split_reduce_kernel<<<(unsigned)((mn + 1023) / 1024), 256, 0, stream>>>(s);
     }
     return hipGetLastError();
 }
