@@ -61,6 +61,9 @@ WORKLOADS = {
 # The same layer sets on FP8-coded operands (apex4_quantize_f8, apex4_gemm_w4a4_f8):
 # name -> the INT4 workload it mirrors
 F8_WORKLOADS = {"llama2-7b-prefill-f8": "llama2-7b-prefill", "llama2-70b-prefill-f8": "llama2-70b-prefill"}
+# Decode with the activation quantization inside the GEMM launch (apex4_linear_w4a4,
+# 1-2 rows): name -> the two-call workload it mirrors
+FUSED_WORKLOADS = {"llama2-70b-decode-m1-fused": "llama2-70b-decode-m1"}
 # Whole-layer workloads (w4a4_group_quantized_amd/linear.py, LlamaLayerW4A4):
 # name -> (description, M, hidden, intermediate)
 LAYER_WORKLOADS = {
@@ -81,7 +84,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2-7b-prefill",
-                    choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS) + sorted(F8_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS) + sorted(F8_WORKLOADS)
+                    + sorted(FUSED_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the GPU's measured ceilings")
@@ -348,9 +352,13 @@ def main():
     from w4a4_group_quantized_amd import apex4
 
     f8 = args.workload in F8_WORKLOADS
-    desc, M, layers, ga, gw, act = WORKLOADS[F8_WORKLOADS.get(args.workload, args.workload)]
+    fused = args.workload in FUSED_WORKLOADS
+    base = F8_WORKLOADS.get(args.workload, FUSED_WORKLOADS.get(args.workload, args.workload))
+    desc, M, layers, ga, gw, act = WORKLOADS[base]
     if f8:
         desc += ", FP8-coded operands (one E4M3 byte per INT4 code)"
+    if fused:
+        desc += ", one apex4_linear_w4a4 call per layer (activation quantization in the GEMM launch where K <= 8192)"
     dev = torch.device("cuda:0")
     apex4.lib()
 
@@ -365,6 +373,8 @@ def main():
         pack = lambda tw: apex4.pack_weight(tw, gw)
         gemm = lambda qa, sa, qw, sw, K, y: apex4.gemm(qa, sa, ga, qw, sw, gw, K, y16=y)
         code_cols = lambda K: K // 2
+    # the one-call form: fp16 rows in, the launch quantizes them itself
+    linear = lambda tx, qw, sw, y: apex4.linear(tx, ga, qw, sw, gw, y16=y)
 
     # --- resident inputs: fp16 activations per layer, weights packed once.
     # Memory-bound workloads cycle through enough independent copies (>= 1 GiB
@@ -388,13 +398,18 @@ def main():
     torch.cuda.synchronize()
 
     ops_step = sum(rl.gemm_ops(M, N, K) for (K, N) in layers)
-    # (FP8-coded operands: one byte per code instead of half)
-    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0) for (K, N) in layers]
+    # (FP8-coded operands: one byte per code instead of half; fused: the fp16
+    # rows are read in place of their codes and scales)
+    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)
+                  + (2 * M * K - M * K / 2 - 4 * M * K / ga if fused else 0) for (K, N) in layers]
 
     def step(i):
         for (K, N, tx, qa, sa, qw, sw, y) in sets[i % copies]:
-            quant(tx, (qa, sa))
-            gemm(qa, sa, qw, sw, K, y)
+            if fused:
+                linear(tx, qw, sw, y)
+            else:
+                quant(tx, (qa, sa))
+                gemm(qa, sa, qw, sw, K, y)
 
     for i in range(args.warmup):
         step(i)
@@ -440,8 +455,11 @@ def main():
     for li, (K, N) in enumerate(layers):
         def gemms():
             for r in range(R):
-                (_, _, _, qa, sa, qw, sw, y) = sets[r % copies][li]
-                gemm(qa, sa, qw, sw, K, y)
+                (_, _, tx, qa, sa, qw, sw, y) = sets[r % copies][li]
+                if fused:
+                    linear(tx, qw, sw, y)
+                else:
+                    gemm(qa, sa, qw, sw, K, y)
         if graphs is not None:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
@@ -500,14 +518,17 @@ def main():
                   "int4 codes on i8 MFMA (i32 sums), f32 rescale"),
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "layers_KN": layers, "group_a": ga, "group_w": gw,
-                   "activations": act, "timed": "quantize_act + gemm per layer",
+                   "activations": act,
+                   "timed": "linear (quantization in the GEMM launch) per layer" if fused
+                   else "quantize_act + gemm per layer",
                    "launch": "eager" if graphs is None else "HIP graph per step",
                    "weight_copies_cycled": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
-                     "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else "gemm (apex4_gemm_w4a4)",
+                     "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else
+                     "fused quantize + gemm (apex4_linear_w4a4)" if fused else "gemm (apex4_gemm_w4a4)",
                      "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3),
                      "measured_ceiling": measured,
                      "frac_of_measured": None if measured is None else achieved / measured},
@@ -600,7 +621,7 @@ def run_layer(args):
             wgraphs.append(gr)
         w4a4_ms = timed(lambda r=0: wgraphs[r % copies].replay(), reps=max(5, copies))
     # GEMM kernel alone per linear, back-to-back launches on the launch stream
-    acts = [lins[0][j]._act_buffers(ins[j].shape[0], dev) for j in range(4)]
+    acts = [apex4.quantize_act(ins[j], g) for j in range(4)]
     gemm_ms = []
     for j, (K, N) in enumerate(shapes):
         def gemms(r=0, j=j, K=K):
@@ -628,7 +649,7 @@ def run_layer(args):
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "hidden": hidden, "intermediate": inter,
                    "layers_KN": shapes, "group_a": g, "group_w": g, "activations": "outlier",
-                   "timed": "LlamaLayerW4A4.forward (quantize_act + gemm per linear, torch ops between)",
+                   "timed": "LlamaLayerW4A4.forward (apex4_linear_w4a4 per linear, torch ops between)",
                    "launch": "eager" if graphs is None else "HIP graph per layer forward",
                    "layers_cycled": copies, "parallelism": "single GPU"},
         "w4a4_ms_per_step": w4a4_ms,

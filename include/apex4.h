@@ -130,6 +130,26 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One W4A4 linear layer call: Y = X * W^T with X quantized on the fly, i.e.
+ * apex4_quantize_act(X) followed by apex4_gemm_w4a4 (the APEX4 page,
+ * Abstract: activations quantized online, weights offline), with the same
+ * codes, scales and result bits as those two calls.  With 1 or 2 rows,
+ * activation groups of 128 or 256 and K <= 8192 the decode kernel quantizes
+ * the rows itself (one launch, no round trip of the codes through memory;
+ * for larger K every workgroup's read of the fp16 rows costs more than the
+ * separate launch); otherwise the quantization runs into the workspace and
+ * the GEMM follows.
+ *   x_f16 [M, K] fp16, 16-byte aligned; qw_u8, s_w, the groups, M, N, K, y_f16
+ *   and y_f32 as in apex4_gemm_w4a4 (no debug sums).
+ *   workspace / workspace_bytes: at least apex4_linear_workspace_size() bytes
+ *   (0 for the fused shapes), 256-byte aligned; caller-owned, overwritten.
+ */
+size_t apex4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w);
+apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* qw_u8, const float* s_w,
+                               int32_t group_w, int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP8-coded operands: a variant of the same GEMM whose operands hold one byte
  * per code instead of two nibbles.  The INT4 codes -8..7 are exact values of
  * FP8 E4M3 (the OCP format of gfx950), and gfx950's FP8 matrix instruction

@@ -1,7 +1,7 @@
 """W4A4Linear and the synthetic LLaMA-shaped layer (w4a4_group_quantized_amd/linear.py)
 against the CPU oracle.
 
-The module runs apex4_quantize_act and apex4_gemm_w4a4; the bar is the one of
+The module runs apex4_linear_w4a4; the bar is the one of
 the GEMM parity tests: packed weight codes and scales bit-exact, fp16 output
 within one fp16 ulp (plus 1e-5 of max|Y_ref|) of fp16(Y_ref).  In the layer,
 every linear is checked on the fp16 input it actually received (the torch
@@ -95,6 +95,88 @@ def test_layer_every_linear_matches_oracle(dev, M):
         assert np.array_equal(getattr(layer, name).qw.cpu().numpy(), qw), name
         check_y16(yi.cpu().numpy(), r32)
     assert layer.linear_shapes() == [(256, 768), (256, 256), (256, 768), (384, 256)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("ga,gw", [(128, 128), (256, 256), (128, "K"), (64, 64), ("K", "K")])
+@pytest.mark.parametrize("M", [1, 2, 3, 16, 300])
+def test_linear_entry_equals_quantize_then_gemm(dev, M, ga, gw):
+    """apex4_linear_w4a4 gives the bits of apex4_quantize_act followed by
+    apex4_gemm_w4a4 (fp16 and fp32 outputs); with 1-2 rows, groups of 128
+    or 256 and K <= 8192 the decode kernel quantizes the rows itself and needs
+    no workspace."""
+    K, N = 1024, 1000
+    ga = K if ga == "K" else ga
+    gw = K if gw == "K" else gw
+    x, w = inputs.problem(M, N, K, seed=M * 7 + ga, act="outlier")
+    tx, tw = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
+    qw, sw = apex4.pack_weight(tw, gw)
+    need = apex4.linear_workspace_size(M, N, K, ga, gw)
+    fused = M <= 2 and ga in (128, 256)
+    assert (need == 0) == fused
+    y16, y32 = apex4.linear(tx, ga, qw, sw, gw, want_y32=True)
+    y16b, y32b = apex4.linear(tx, ga, qw, sw, gw, want_y32=True)
+    qa, sa = apex4.quantize_act(tx, ga)
+    r16, r32, _ = apex4.gemm(qa, sa, ga, qw, sw, gw, K, want_y32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.view(torch.int32), r32.view(torch.int32))
+    assert torch.equal(y16.view(torch.int16), r16.view(torch.int16))
+    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32))
+    if M <= 16:
+        _, _, o32 = oracle_linear(x, w, ga, gw)
+        check_y16(y16.cpu().numpy(), o32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 2])
+def test_linear_large_k_two_launches(dev, M):
+    """K = 9216 > 8192: quantization into the workspace, then the GEMM; the
+    same bits as the two calls."""
+    K, N = 9216, 520
+    x, w = inputs.problem(M, N, K, seed=M, act="student_t")
+    tx, tw = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
+    qw, sw = apex4.pack_weight(tw, 128)
+    assert apex4.linear_workspace_size(M, N, K, 128, 128) > 0
+    y16, y32 = apex4.linear(tx, 128, qw, sw, 128, want_y32=True)
+    qa, sa = apex4.quantize_act(tx, 128)
+    r16, r32, _ = apex4.gemm(qa, sa, 128, qw, sw, 128, K, want_y32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.view(torch.int32), r32.view(torch.int32))
+    assert torch.equal(y16.view(torch.int16), r16.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_linear_fused_full_70b_decode(dev):
+    """The fused decode launch at the 70B up-projection shape (M=1, K=8192,
+    N=28672), sampled output columns against the oracle."""
+    M, K, N = 1, 8192, 28672
+    x, w = inputs.problem(M, N, K, seed=4, act="outlier")
+    tx, tw = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
+    qw, sw = apex4.pack_weight(tw, 128)
+    y16, y32 = apex4.linear(tx, 128, qw, sw, 128, want_y32=True)
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 63, 64, 4095, 15000, 28670, 28671])
+    oqa, osa = orc.quantize(x, 128)
+    oqw, osw = orc.quantize(w[cols], 128)
+    _, o32, _ = orc.gemm(oqa, osa, 128, oqw, osw, 128, K)
+    got = y32.cpu().numpy()[:, cols].astype(np.float64)
+    assert float(np.abs(got - o32).max()) <= REL_TOL * float(np.abs(o32).max())
+
+
+@pytest.mark.gpu
+def test_linear_argument_checks(dev):
+    x = torch.zeros((40, 256), dtype=torch.float16, device=dev)
+    qw = torch.zeros((64, 128), dtype=torch.uint8, device=dev)
+    sw = torch.ones((64, 2), dtype=torch.float32, device=dev)
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(apex4.Apex4Error):
+        apex4.linear(x, 128, qw, sw, 128, workspace=small)        # workspace too small
+    with pytest.raises(apex4.Apex4Error):
+        apex4.linear(x, 96, qw, sw, 96)                           # unsupported group
+    assert apex4.linear_workspace_size(40, 64, 256, 128, 128) > 0
+    assert apex4.linear_workspace_size(1, 64, 256, 128, 128) == 0
+    assert apex4.linear_workspace_size(1, 64, 200, 128, 128) == 0   # invalid: 0, and the call refuses
+    assert apex4.linear_workspace_size(1, 64, 16384, 128, 128) > 0  # K > 8192: two launches
 
 
 def test_linear_refuses_host_tensors():

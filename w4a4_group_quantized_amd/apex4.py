@@ -30,6 +30,8 @@ SIGNATURES = {
     "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
+    "apex4_linear_w4a4": (_I32, [_P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "apex4_gemm_w4a4_f8": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
@@ -148,6 +150,36 @@ def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bo
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16
+
+
+def linear_workspace_size(M: int, N: int, K: int, ga: int, gw: int) -> int:
+    return int(lib().apex4_linear_workspace_size(M, N, K, ga, gw))
+
+
+def linear(x, ga: int, qw, sw, gw: int, *, want_y32: bool = False, y16=None, y32=None, workspace=None):
+    """apex4_linear_w4a4: Y of quantize_act(x) then gemm in one call (the decode
+    kernel quantizes 1-2 rows itself).  x: fp16 [M, K]; returns y16, or
+    (y16, y32) with want_y32.  `workspace`: a uint8 GPU tensor of at least
+    linear_workspace_size() bytes (allocated here when None)."""
+    import torch
+    _need_gpu(x, "x", torch.float16)
+    _need_gpu(qw, "qw", torch.uint8)
+    _need_gpu(sw, "s_w", torch.float32)
+    M, K = x.shape
+    N = qw.shape[0]
+    dev = x.device
+    if y16 is None:
+        y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if want_y32 and y32 is None:
+        y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    need = linear_workspace_size(M, N, K, ga, gw)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check("apex4_linear_w4a4", lib().apex4_linear_w4a4(
+        _ptr(x), ga, _ptr(qw), _ptr(sw), gw, M, N, K, _ptr(y16), _ptr(y32), _ptr(workspace), nbytes,
+        _stream(torch, dev)))
+    return (y16, y32) if want_y32 else y16
 
 
 def quantize_f8(x, group: int = 128, out=None):

@@ -65,6 +65,73 @@ apex4_status apex4_pack_weight(const void* w_f16, int64_t N, int64_t K, int32_t 
                                             static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// the GEMM problem of a linear call (shape and groups only), or false
+bool linear_problem(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w, apex4::GemmProblem& p)
+{
+    if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0) return false;
+    if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return false;
+    p = apex4::GemmProblem{};
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.ga = group_a;
+    p.gw = group_w;
+    return true;
+}
+
+}  // namespace
+
+size_t apex4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w)
+{
+    apex4::GemmProblem p;
+    if (!linear_problem(M, N, K, group_a, group_w, p)) return 0;
+    if (apex4::gemv_fused_supports(p)) return 0;
+    return align256((size_t)M * (K / 2)) + align256((size_t)M * (K / group_a) * 4) + apex4::gemm_workspace_bytes(p);
+}
+
+apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* qw_u8, const float* s_w,
+                               int32_t group_w, int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    // the checks of apex4_quantize_act and apex4_gemm_w4a4
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return APEX4_ERR_INVALID_ARG;
+    if (!small_group(group_a) && group_a != K) return APEX4_ERR_UNSUPPORTED;
+    if (!(group_w == group_a || group_w == K)) return APEX4_ERR_UNSUPPORTED;
+    const size_t need = apex4_linear_workspace_size(M, N, K, group_a, group_w);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return APEX4_ERR_WORKSPACE;
+    if (M == 0 || N == 0) return APEX4_OK;
+    if (!x_f16 || !qw_u8 || !s_w || !y_f16) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(x_f16, 16) || !aligned(qw_u8, 16) || !aligned(s_w, 4) || !aligned(y_f16, 2) ||
+        !aligned(y_f32, 4) || !aligned(workspace, 256))
+        return APEX4_ERR_ALIGNMENT;
+    apex4::GemmProblem p;
+    linear_problem(M, N, K, group_a, group_w, p);
+    p.qw = static_cast<const uint8_t*>(qw_u8);
+    p.sw = s_w;
+    p.y16 = y_f16;
+    p.y32 = y_f32;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (apex4::gemv_fused_supports(p)) return to_status(apex4::launch_gemm_gemv_fused(p, x_f16, st));
+    // quantize into the workspace, then the GEMM (its own workspace after)
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const size_t qa_bytes = align256((size_t)M * (K / 2)), sa_bytes = align256((size_t)M * (K / group_a) * 4);
+    uint8_t* qa = ws;
+    float* sa = reinterpret_cast<float*>(ws + qa_bytes);
+    hipError_t e = apex4::launch_quantize(x_f16, M, K, group_a, qa, sa, st);
+    if (e != hipSuccess) return APEX4_ERR_HIP;
+    p.qa = qa;
+    p.sa = sa;
+    p.ws = ws + qa_bytes + sa_bytes;
+    p.ws_bytes = workspace_bytes - qa_bytes - sa_bytes;
+    return to_status(apex4::launch_gemm(p, st));
+}
+
 apex4_status apex4_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q8,
                                float* s, void* stream)
 {

@@ -32,6 +32,7 @@
 // of its unit starting at quad (l >> 1) & 3, for activations and weights
 // alike, so that 8 consecutive lanes hit distinct LDS banks.
 #include "internal.h"
+#include "quant_rule.h"
 
 namespace apex4 {
 namespace {
@@ -56,6 +57,7 @@ struct GemvArgs {
     int G;             // K / gs
     int U;             // units per row: K / 128
     int lds_qa;        // bytes of activation rows in LDS: M * K/2, 16-byte multiple
+    const _Float16* x; // fused quantization: the fp16 activation rows [M, K]
     _Float16* y16;
     float* y32;
     int32_t* psum;
@@ -83,8 +85,10 @@ __device__ inline int wave_sum_int(int v)
 
 // MR: activation rows handled (M <= MR).  GM: 1 (groups of 128), 2 (groups of
 // 256) or 0 (one group over K).  MIXED: per-channel weight scales with
-// activation groups of 128.
-template <int MR, int GM, bool MIXED, bool DEBUG_P>
+// activation groups of 128.  FUSED: the workgroup quantizes the fp16
+// activation rows itself (groups of 128 or 256), by the rule of the
+// quantization kernels, into the LDS layout the copy would fill.
+template <int MR, int GM, bool MIXED, bool DEBUG_P, bool FUSED = false>
 __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -118,17 +122,58 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
         ws[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                  rS, live ? (int)(((uint32_t)n * a.Gw + j) * 4) : (int)OOB, 0, 0));
     };
+    // (the fused prologue's activation loads go out first, ahead of the weights)
+    if constexpr (!FUSED) {
 #pragma unroll
-    for (int k = 0; k < PF - 1; ++k) issue(k, k);
+        for (int k = 0; k < PF - 1; ++k) issue(k, k);
+    }
 
     // --- activation rows (rows past M zero) and their scales into LDS ---
     float* lsa = reinterpret_cast<float*>(lds + MR * rowbytes);
-    {
+    if constexpr (FUSED) {
+        // chunk c (8 values) of the MR rows: word c of the packed codes, a
+        // group of TPG consecutive chunks (consecutive lanes of one wave); every
+        // lane runs every pass, so the groups' lane exchanges see full waves.
+        // NB passes' loads are issued before any is used (one L2 round trip
+        // per NB passes); chunks of rows past M read as zero (out-of-range
+        // buffer offsets).
+        using namespace qrule;
+        typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+        constexpr int TPG = (GM == 2 ? 256 : 128) / 8, NB = 8;
+        const int k8 = a.K / 8, n8 = MR * k8, live8 = a.M * k8;
+        const __amdgpu_buffer_rsrc_t rX = buffer_of(a.x, (uint32_t)live8 * 16);
+        uint32_t* dq = reinterpret_cast<uint32_t*>(lds);
+        for (int c0 = 0; c0 < n8; c0 += NB * THREADS) {
+            half8 h[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int c = c0 + b * THREADS + tid;
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rX, c < live8 ? c * 16 : (int)OOB, 0, 0);
+                h[b] = __builtin_bit_cast(half8, v);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int c = c0 + b * THREADS + tid;
+                const float amax = group_max<TPG>(absmax8(h[b]));
+                const float scale = amax / 7.0f;
+                const bool nz = amax != 0.0f;
+                const uint32_t word = quantize8(h[b], scale, nz);
+                if (c < n8) {
+                    dq[c] = word;
+                    if (c % TPG == 0) lsa[c / TPG] = nz ? scale : 0.0f;
+                }
+            }
+        }
+    } else {
         const uint4* src = reinterpret_cast<const uint4*>(a.qa);
         uint4* dst = reinterpret_cast<uint4*>(lds);
         const int nq = MR * (int)rowbytes / 16, live_q = a.lds_qa / 16;
         for (int i = tid; i < nq; i += THREADS) dst[i] = i < live_q ? src[i] : make_uint4(0, 0, 0, 0);
         for (int i = tid; i < MR * a.Ga; i += THREADS) lsa[i] = i < a.M * a.Ga ? a.sa[i] : 0.0f;
+    }
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int k = 0; k < PF - 1; ++k) issue(k, k);
     }
     __syncthreads();
 
@@ -206,22 +251,28 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
 }
 
 template <int MR>
-hipError_t launch_mr(const GemvArgs& g, int gm, bool mixed, bool dbg, hipStream_t stream)
+hipError_t launch_mr(const GemvArgs& g, int gm, bool mixed, bool dbg, hipStream_t stream, bool fused = false)
 {
     const int blocks = (g.N + WAVES - 1) / WAVES < 256 ? (g.N + WAVES - 1) / WAVES : 256;
     const size_t lds = (size_t)MR * g.K / 2 + (size_t)MR * g.Ga * 4;
     // dynamic LDS above 64 KB has to be allowed per kernel
-#define APEX4_GEMV(GM_, MX, DB)                                                                  \
+#define APEX4_GEMV_K(GM_, MX, DB, FU)                                                            \
     do {                                                                                        \
         if (lds > 65536) {                                                                      \
             const hipError_t e = hipFuncSetAttribute(                                           \
-                reinterpret_cast<const void*>(&gemm_gemv_kernel<MR, GM_, MX, DB>),              \
+                reinterpret_cast<const void*>(&gemm_gemv_kernel<MR, GM_, MX, DB, FU>),          \
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                          \
             if (e != hipSuccess) return e;                                                      \
         }                                                                                       \
-        gemm_gemv_kernel<MR, GM_, MX, DB><<<blocks, THREADS, lds, stream>>>(g);                 \
+        gemm_gemv_kernel<MR, GM_, MX, DB, FU><<<blocks, THREADS, lds, stream>>>(g);             \
     } while (0)
-    if (mixed) {
+#define APEX4_GEMV(GM_, MX, DB) APEX4_GEMV_K(GM_, MX, DB, false)
+    if (fused) {
+        // (groups of 128 or 256, mixed with 128; no debug sums)
+        if (mixed) APEX4_GEMV_K(1, true, false, true);
+        else if (gm == 2) APEX4_GEMV_K(2, false, false, true);
+        else APEX4_GEMV_K(1, false, false, true);
+    } else if (mixed) {
         if (dbg) APEX4_GEMV(1, true, true);
         else APEX4_GEMV(1, true, false);
     } else if (gm == 1) {
@@ -235,6 +286,7 @@ hipError_t launch_mr(const GemvArgs& g, int gm, bool mixed, bool dbg, hipStream_
         else APEX4_GEMV(0, false, false);
     }
 #undef APEX4_GEMV
+#undef APEX4_GEMV_K
     return hipGetLastError();
 }
 
@@ -260,9 +312,48 @@ bool gemv_supports(const GemmProblem& p)
     return wbytes < OOB && sbytes < OOB && lds <= 160 * 1024;
 }
 
+bool gemv_fused_supports(const GemmProblem& p)
+{
+    // the row-streaming kernel with 1 or 2 rows, activation groups of 128 or
+    // 256 (one group over K would need a row-wide maximum first), K up to
+    // 8192: every workgroup reads the fp16 rows (4x the bytes of their codes)
+    // before its weight stream starts, and at the per-CU fetch rate of the
+    // stream that costs more than the separate quantization launch beyond
+    // that (70B down-projection, K = 28672: 27.3 us fused, 25.8 us as two
+    // launches; up-projection, K = 8192: 24.8 us and 24.9 us)
+    return p.M >= 1 && p.M <= 2 && p.K <= 8192 && gemv_supports(p) && (p.ga == UNIT || p.ga == 2 * UNIT);
+}
+
+hipError_t launch_gemm_gemv_fused(const GemmProblem& p, const void* x_f16, hipStream_t stream)
+{
+    GemvArgs g{};
+    g.qa = nullptr;
+    g.sa = nullptr;
+    g.x = static_cast<const _Float16*>(x_f16);
+    g.qw = p.qw;
+    g.sw = p.sw;
+    g.M = p.M;
+    g.N = p.N;
+    g.K = p.K;
+    g.Ga = p.K / p.ga;
+    g.Gw = p.K / p.gw;
+    g.ga = p.ga;
+    const int gs = p.ga < p.gw ? p.ga : p.gw;
+    g.G = p.K / gs;
+    g.U = p.K / UNIT;
+    g.lds_qa = p.M * (p.K / 2);
+    g.y16 = static_cast<_Float16*>(p.y16);
+    g.y32 = p.y32;
+    g.psum = nullptr;
+    const bool mixed = p.gw == p.K && p.ga != p.gw;
+    const int gm = gs == 2 * UNIT ? 2 : 1;
+    if (p.M == 1) return launch_mr<1>(g, gm, mixed, false, stream, true);
+    return launch_mr<2>(g, gm, mixed, false, stream, true);
+}
+
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream)
 {
-    GemvArgs g;
+    GemvArgs g{};
     g.qa = p.qa;
     g.sa = p.sa;
     g.qw = p.qw;

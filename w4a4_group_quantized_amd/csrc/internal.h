@@ -61,6 +61,9 @@ hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* 
                               hipStream_t stream);
 bool gemv_supports(const GemmProblem& p);
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);
+// the row-streaming kernel quantizing its (1 or 2) fp16 activation rows itself
+bool gemv_fused_supports(const GemmProblem& p);
+hipError_t launch_gemm_gemv_fused(const GemmProblem& p, const void* x_f16, hipStream_t stream);
 bool stream_supports(const GemmProblem& p);
 hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);
 bool kouter_supports(const GemmProblem& p);

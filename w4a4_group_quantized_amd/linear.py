@@ -4,8 +4,9 @@ The APEX4 page (aiqbench news page, Abstract) presents the method as a
 drop-in replacement for a model's linear layers: weights quantized ahead of
 time to INT4 with per-group scales, activations quantized on the fly, one
 W4A4 GEMM with per-group dequantization.  `W4A4Linear` is that layer over the
-library's C ABI (include/apex4.h): `forward` runs apex4_quantize_act and
-apex4_gemm_w4a4 on torch's current stream, nothing else.
+library's C ABI (include/apex4.h): `forward` runs apex4_linear_w4a4 (the
+activation quantization and the GEMM; for 1-2 rows one fused launch) on
+torch's current stream, nothing else.
 
 `LlamaLayerW4A4` strings four of them together the way one LLaMA decoder layer
 uses its linear layers (fused QKV, O, fused gate+up, down) with random
@@ -30,9 +31,9 @@ class W4A4Linear(torch.nn.Module):
     (apex4_pack_weight's outputs), group_a: activation group size used by the
     on-the-fly quantization (group_w == group_a, or group_w == K for
     per-channel weight scales with activation groups).  Inputs: fp16
-    [..., K] on the GPU; output fp16 [..., N].  The activation code/scale
-    buffers are kept per row count, so repeated calls at one shape allocate
-    only the output.
+    [..., K] on the GPU; output fp16 [..., N].  The call's workspace (the
+    activation codes and scales, and the GEMM's K-split partials) is kept per
+    row count, so repeated calls at one shape allocate only the output.
     """
 
     def __init__(self, qw: torch.Tensor, sw: torch.Tensor, group_w: int, group_a: int | None = None):
@@ -45,7 +46,7 @@ class W4A4Linear(torch.nn.Module):
         self.group_a = group_w if group_a is None else group_a
         self.register_buffer("qw", qw)
         self.register_buffer("sw", sw)
-        self._act = {}
+        self._ws = {}
 
     @classmethod
     def from_weight(cls, w: torch.Tensor, group_w: int = 128, group_a: int | None = None) -> "W4A4Linear":
@@ -53,14 +54,13 @@ class W4A4Linear(torch.nn.Module):
         qw, sw = apex4.pack_weight(w.contiguous(), group_w)
         return cls(qw, sw, group_w, group_a)
 
-    def _act_buffers(self, M: int, device):
-        buf = self._act.get(M)
-        if buf is None:
-            K = self.in_features
-            buf = (torch.empty((M, K // 2), dtype=torch.uint8, device=device),
-                   torch.empty((M, K // self.group_a), dtype=torch.float32, device=device))
-            self._act[M] = buf
-        return buf
+    def _workspace(self, M: int, device):
+        ws = self._ws.get(M)
+        if ws is None:
+            need = apex4.linear_workspace_size(M, self.out_features, self.in_features, self.group_a, self.group_w)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+            self._ws[M] = ws
+        return ws
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         if x.shape[-1] != self.in_features:
@@ -70,9 +70,9 @@ class W4A4Linear(torch.nn.Module):
         if not x2.is_contiguous():
             x2 = x2.contiguous()
         M = x2.shape[0]
-        qa, sa = apex4.quantize_act(x2, self.group_a, out=self._act_buffers(M, x2.device))
-        y = apex4.gemm(qa, sa, self.group_a, self.qw, self.sw, self.group_w, self.in_features,
-                       y16=None if out is None else out.reshape(M, self.out_features))
+        y = apex4.linear(x2, self.group_a, self.qw, self.sw, self.group_w,
+                         y16=None if out is None else out.reshape(M, self.out_features),
+                         workspace=self._workspace(M, x2.device))
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:
