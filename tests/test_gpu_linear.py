@@ -188,11 +188,13 @@ def test_linear_refuses_host_tensors():
 
 
 @pytest.mark.gpu
-def test_layer_graph_replays_match_eager(dev):
+@pytest.mark.parametrize("M", [16, 1])
+def test_layer_graph_replays_match_eager(dev, M):
     """The layer forward captured as one HIP graph: every replay, with eager
-    work and synchronizations between them, gives the eager result bit for bit."""
+    work and synchronizations between them, gives the eager result bit for bit
+    (M = 1: every linear is one fused launch)."""
     layer = LlamaLayerW4A4.random(256, 384, 128, seed=5, device=dev)
-    x = torch.from_numpy(inputs.activations(np.random.default_rng(9), 16, 256, "outlier", 9)).to(dev)
+    x = torch.from_numpy(inputs.activations(np.random.default_rng(9), M, 256, "outlier", 9)).to(dev)
     ref = layer(x).clone()                      # eager (also allocates the activation buffers)
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
