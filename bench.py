@@ -101,7 +101,7 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
                          "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
@@ -272,7 +272,9 @@ def write_traffic(prof_dir, workloads):
                           "bench.py reports them only while the sources of the workload's kernels hash the same.",
            "calibration": cal, "workloads": {}}
     for wl in workloads:
-        _, M, layers, ga, gw, _ = WORKLOADS[wl]
+        # (FP8-coded operands: one byte per code, (M + N) K / 2 more bytes read)
+        f8 = wl in F8_WORKLOADS
+        _, M, layers, ga, gw, _ = WORKLOADS[F8_WORKLOADS.get(wl, wl)]
         fc, wc = step_calls("FETCH_SIZE", wl), step_calls("WRITE_SIZE", wl)
         names = {k for ks, _ in fc for k in ks}
         files = kernel_source_files(names)
@@ -284,7 +286,7 @@ def write_traffic(prof_dir, workloads):
             per.append({"M": M, "K": K, "N": N, "dispatches": len(f),
                         "fetch_bytes": sum(f) / len(f) * 1024 * cal["fetch_factor"],
                         "write_bytes": sum(w) / len(w) * 1024 * cal["write_factor"],
-                        "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw)})
+                        "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)})
         out["workloads"][wl] = {
             "kernel_sources": files,
             "kernel_sources_sha256": kernel_sources_sha256(files),
