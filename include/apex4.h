@@ -142,7 +142,16 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
  *   x_f16 [M, K] fp16, 16-byte aligned; qw_u8, s_w, the groups, M, N, K, y_f16
  *   and y_f32 as in apex4_gemm_w4a4 (no debug sums).
  *   workspace / workspace_bytes: at least apex4_linear_workspace_size() bytes
- *   (0 for the fused shapes), 256-byte aligned; caller-owned, overwritten.
+ *   (0 for the fused shapes), 256-byte aligned; caller-owned, overwritten
+ *   (the activation codes, then their scales, each part 256-byte aligned,
+ *   then the GEMM's own workspace); calls that share one workspace race.
+ *   Errors: APEX4_ERR_INVALID_ARG (shapes, groups, null pointers),
+ *   APEX4_ERR_UNSUPPORTED (a group combination the quantizer or the GEMM does
+ *   not run), APEX4_ERR_ALIGNMENT, APEX4_ERR_WORKSPACE, APEX4_ERR_HIP; all
+ *   but the last are found on the host before anything is enqueued.  M == 0
+ *   or N == 0 is a no-op.  The work is enqueued on `stream` and the call
+ *   returns before it runs.  apex4_linear_workspace_size returns 0 for
+ *   invalid arguments (the call then reports them).
  */
 size_t apex4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w);
 apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* qw_u8, const float* s_w,
