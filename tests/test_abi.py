@@ -110,6 +110,49 @@ def test_gemm_validation(L):
     assert _gemm(L, N=0, qw=None, sw=None, y16=None) == OK
 
 
+def test_linear_workspace_layout(L):
+    """apex4_linear_workspace_size: 0 for the fused decode shapes; otherwise
+    the activation codes, then their scales (each 256-byte aligned), then the
+    GEMM's own workspace.  (Host arithmetic; the ping-pong split's share
+    depends on the device's compute units, so it is taken from
+    apex4_gemm_workspace_size in the same process.)"""
+    assert L.apex4_linear_workspace_size(1, 28672, 8192, 128, 128) == 0
+    assert L.apex4_linear_workspace_size(2, 28672, 8192, 256, 256) == 0
+
+    def a256(b):
+        return (b + 255) // 256 * 256
+    for M, N, K, ga, gw in [(1, 8192, 28672, 128, 128), (2, 512, 1024, 1024, 1024), (3, 1000, 1024, 64, 64),
+                            (40, 8192, 28672, 128, 128), (300, 1000, 1024, 128, 1024)]:
+        expect = a256(M * K // 2) + a256(M * (K // ga) * 4) + L.apex4_gemm_workspace_size(M, N, K, ga, gw)
+        assert L.apex4_linear_workspace_size(M, N, K, ga, gw) == expect, (M, N, K, ga, gw)
+    # the K-outer kernel's two K halves (17-64 rows, at most 2 column blocks per workgroup)
+    assert L.apex4_gemm_workspace_size(40, 8192, 28672, 128, 128) == 2 * 40 * 8192 * 4
+    # invalid arguments: 0 (the call itself reports them)
+    assert L.apex4_linear_workspace_size(1, 64, 200, 128, 128) == 0
+    assert L.apex4_linear_workspace_size(0, 64, 256, 128, 128) == 0
+
+
+def _linear(L, x=A16, ga=128, qw=A16, sw=A16b, gw=128, M=1, N=16, K=1024, y16=A16b, y32=None, ws=None, wsb=0):
+    return L.apex4_linear_w4a4(x, ga, qw, sw, gw, M, N, K, y16, y32, ws, wsb, None)
+
+
+def test_linear_validation(L):
+    assert _linear(L, K=1000) == INVALID               # K % 128
+    assert _linear(L, ga=96, gw=96) == INVALID         # does not divide K
+    assert _linear(L, ga=512, gw=512) == UNSUPPORTED   # not in {32..256, K}
+    assert _linear(L, ga=128, gw=64) == UNSUPPORTED    # neither equal nor mixed
+    assert _linear(L, M=40, N=8192, K=28672) == WORKSPACE     # needs the codes, scales and K halves
+    assert _linear(L, M=40, N=8192, K=28672, ws=A16, wsb=1000) == WORKSPACE
+    assert _linear(L, x=None) == INVALID
+    assert _linear(L, y16=None) == INVALID
+    assert _linear(L, x=MIS) == ALIGN
+    assert _linear(L, y32=A16b + 2) == ALIGN
+    assert _linear(L, M=3, ws=A16 + 16, wsb=1 << 20) == ALIGN   # workspace not 256-byte aligned
+    # empty shapes are successful no-ops
+    assert _linear(L, M=0, x=None, y16=None) == OK
+    assert _linear(L, N=0, qw=None, sw=None, y16=None) == OK
+
+
 def test_probe_validation(L):
     """The probes check their arguments on the host (nothing is launched)."""
     d = ctypes.c_double(0.0)
