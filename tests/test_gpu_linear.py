@@ -77,6 +77,27 @@ def test_linear_leading_dims_and_new_row_counts(dev):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 24])
+def test_linear_out_buffer_and_strided_input(dev, M):
+    """`out=` is written in place and returned; a non-contiguous input (every
+    other column of a wider tensor) gives the bits of its contiguous copy."""
+    x, w = inputs.problem(M, 384, 512, seed=21 + M, act="outlier")
+    lin = W4A4Linear.from_weight(torch.from_numpy(w).to(dev), 128)
+    wide = torch.zeros((M, 1024), dtype=torch.float16, device=dev)
+    wide[:, ::2] = torch.from_numpy(x).to(dev)
+    view = wide[:, ::2]
+    assert not view.is_contiguous()
+    out = torch.empty((M, 384), dtype=torch.float16, device=dev)
+    y = lin(view, out=out)
+    ref = lin(view.contiguous())
+    torch.cuda.synchronize()
+    assert y.data_ptr() == out.data_ptr()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    _, _, r32 = oracle_linear(x, w, 128, 128)
+    check_y16(out.cpu().numpy(), r32)
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("M", [40, 3])
 def test_layer_every_linear_matches_oracle(dev, M):
     hidden, inter, g = 256, 384, 128
