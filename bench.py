@@ -72,6 +72,10 @@ LAYER_WORKLOADS = {
                                 "residual adds and SwiGLU as torch ops), M=2048, g=128", 2048, 4096, 11008),
     "llama2-7b-layer-decode-m16": ("the same layer at M=16 (decode)", 16, 4096, 11008),
 }
+# The small case (0.6 MB, 34 Mop): bound by launch latency, not by either roofline;
+# its absolute time per call is the figure (per_layer gemm_us)
+WORKLOADS["tiny"] = ("tiny case M=16, K=N=1024, g=128 (launch-latency bound: read the absolute time)",
+                     16, [(1024, 1024)], 128, 128, "normal")
 for _M in (1, 4, 16, 64):
     WORKLOADS[f"llama2-70b-decode-m{_M}"] = (
         f"LLaMA-2-70B-shaped decode, M={_M}: up-proj (K=8192, N=28672) and down-proj "
@@ -121,6 +125,18 @@ def calibrate_copy():
                       "gbs_read_plus_write": 2 * n / dt / 1e9}))
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
     """Time the CPU oracle (quantize + GEMM) on the first rows of every layer.
 
@@ -159,6 +175,7 @@ def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
         "value": total_ops / total_s / 1e12,
         "unit": "TOPS",
         "cores": o.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"first {rows} of {M} rows of every layer (quantize + GEMM, weights "
                   f"pre-packed), {total_s:.1f} s",
@@ -384,7 +401,8 @@ def main():
     # than from the 256 MB last-level cache.
     bound = rl.bound_of(M, layers[0][1], layers[0][0], ga, gw)
     set_bytes = sum(rl.gemm_bytes(M, N, K, ga, gw) for (K, N) in layers)
-    copies = 1 if bound == "mfma" else max(2, int(np.ceil(2**30 / set_bytes)))
+    # (the launch-bound tiny case: one copy, its time is latency either way)
+    copies = 1 if bound == "mfma" or base == "tiny" else max(2, int(np.ceil(2**30 / set_bytes)))
     sets = []
     for c in range(copies):
         data = []
