@@ -15,14 +15,14 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound: 1507/2231 = 0.675 >= 0.65 > 815/2231 = 0.37
+    # compute-bound: 1565/2316 = 0.676 >= 0.65 > 817/2316 = 0.35
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # mixed 1661/2231 = 0.745 qualifies at 0.72 (g=128, 0.675, does not);
-    # at 0.75 neither mixed nor g=256 (0.686) does
-    assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (128, 8192)
+    # mixed 1672/2316 = 0.722 qualifies at 0.70 (g=128, 0.676, does not);
+    # at 0.75 neither mixed nor g=256 (1674/2316 = 0.723) does
+    assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 

@@ -484,7 +484,6 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         // (t and h have the same parity)
         const bool zero = SPG == 1 || (SPG == 2 && h == 0);   // stage t starts a group
         const bool ends = SPG == 1 || (SPG == 2 && h == 1);   // stage t ends a group
-        const bool prev_ends = SPG == 1 || (SPG == 2 && h == 0);   // stage t-1 ended one
         const int grp = SPG == 2 ? t >> 1 : t;                // the group of stage t
         // The copy runs in every stage, also past the last one: loads past the
         // end of K read other rows or zeros, and the stores go to a buffer
@@ -518,37 +517,36 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             mma_stage(h, zero, ends);
             store_stage(h ^ 1, h ^ 1);
             lds_barrier();
-        } else if (EARLY) {
-            // phase 1: matrix work of stage t, copy of stage t+1
+        } else if (SPG == 2) {
+            // Groups of two stages: one rescale per two stages leaves the
+            // ping-pong's vector phase empty half the time, so here too both
+            // wave groups run the matrix work of every stage together (the
+            // stored registers freed before the MFMAs, as P stays live across
+            // the group's two stages), and every wave rescales the group
+            // after the barrier of its second stage.
             load_stage(t + 2, h);
-            if (SPG == 2) {
-                // groups of two stages: the stored registers freed before the
-                // MFMAs (P stays live across stages here)
-                store_stage(h ^ 1, h ^ 1);
-                mma_stage(h, zero, ends);
-            } else {
-                mma_stage(h, zero, ends);
-                store_stage(h ^ 1, h ^ 1);
-            }
+            store_stage(h ^ 1, h ^ 1);
+            mma_stage(h, zero, ends);
             lds_barrier();
-            // phase 2: rescale of stage t's group when the stage ends it
             if (ends) rescale(grp);
+        } else if (EARLY) {
+            // groups of one stage, ping-pong.  Phase 1: matrix work of stage
+            // t, copy of stage t+1
+            load_stage(t + 2, h);
+            mma_stage(h, true, true);
+            store_stage(h ^ 1, h ^ 1);
+            lds_barrier();
+            // phase 2: rescale of stage t's group
+            rescale(t);
             lds_barrier();
         } else {
-            // phase 1: rescale of stage t-1's group when that stage ended it
-            if (prev_ends && t > 0) rescale(SPG == 2 ? (t - 1) >> 1 : t - 1);
+            // phase 1: rescale of stage t-1's group
+            if (t > 0) rescale(t - 1);
             lds_barrier();
             // phase 2: matrix work of stage t, copy of stage t+1
             load_stage(t + 2, h);
-            if (SPG == 2) {
-                // groups of two stages: the stored registers freed before the
-                // MFMAs (P stays live across stages here)
-                store_stage(h ^ 1, h ^ 1);
-                mma_stage(h, zero, ends);
-            } else {
-                mma_stage(h, zero, ends);
-                store_stage(h ^ 1, h ^ 1);
-            }
+            mma_stage(h, true, true);
+            store_stage(h ^ 1, h ^ 1);
             lds_barrier();
         }
         }
@@ -558,7 +556,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         // scales are the same in every stage)
         scale_products((stages - 1) & 1);
         rescale(0);
-    } else if (!EARLY) {
+    } else if (!EARLY && SPG == 1) {
         // the last stage ends the last group
         rescale(a.G - 1);
     }

@@ -23,12 +23,12 @@ struct Mode {
 // outliers), then weight groups.  Rates: bench.py --workload sweep-*, GEMM
 // alone (roofline.achieved), Student-t activations, all six on one GPU.
 constexpr Mode kModes[] = {
-    {32, 32, 484e12},
-    {64, 64, 815e12},
-    {128, 128, 1507e12},
-    {128, 0, 1661e12},    // mixed: per-channel weights, activation groups of 128
-    {256, 256, 1531e12},
-    {0, 0, 2231e12},      // per-channel on both operands
+    {32, 32, 485e12},
+    {64, 64, 817e12},
+    {128, 128, 1565e12},
+    {128, 0, 1672e12},    // mixed: per-channel weights, activation groups of 128
+    {256, 256, 1674e12},
+    {0, 0, 2316e12},      // per-channel on both operands
 };
 
 // the weight-streaming rate the decode kernels reach (4.2-5.4 TB/s measured)
