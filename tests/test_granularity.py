@@ -21,9 +21,10 @@ def test_prefill_picks_g128_at_65_percent():
 
 def test_prefill_tighter_budgets_coarsen():
     # mixed 1672/2316 = 0.722 qualifies at 0.70 (g=128, 0.676, does not);
-    # at 0.75 neither mixed nor g=256 (1674/2316 = 0.723) does
+    # at 0.75 only g=256 (1750/2316 = 0.756) and coarser do; at 0.8 only g=K
     assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.80) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 
 

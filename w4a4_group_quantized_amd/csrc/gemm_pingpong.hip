@@ -520,13 +520,19 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         } else if (SPG == 2) {
             // Groups of two stages: one rescale per two stages leaves the
             // ping-pong's vector phase empty half the time, so here too both
-            // wave groups run the matrix work of every stage together (the
-            // stored registers freed before the MFMAs, as P stays live across
-            // the group's two stages), and every wave rescales the group
-            // after the barrier of its second stage.
+            // wave groups run the matrix work of every stage together, and
+            // every wave rescales the group after the barrier of its second
+            // stage.  The first stage stores its copy after the MFMAs (as for
+            // one group over K); in the second, P is live from the first, so
+            // the stored registers are freed before the MFMAs.
             load_stage(t + 2, h);
-            store_stage(h ^ 1, h ^ 1);
-            mma_stage(h, zero, ends);
+            if (h == 0) {
+                mma_stage(h, zero, ends);
+                store_stage(h ^ 1, h ^ 1);
+            } else {
+                store_stage(h ^ 1, h ^ 1);
+                mma_stage(h, zero, ends);
+            }
             lds_barrier();
             if (ends) rescale(grp);
         } else if (EARLY) {
