@@ -45,7 +45,7 @@ typedef int32_t apex4_status;
 
 #define APEX4_OK 0
 #define APEX4_ERR_INVALID_ARG 1  /* a size or pointer is out of the documented range */
-#define APEX4_ERR_UNSUPPORTED 2  /* a group-size combination this build does not run */
+#define APEX4_ERR_UNSUPPORTED 2  /* a group-size combination this library does not run */
 #define APEX4_ERR_ALIGNMENT 3    /* a pointer lacks the documented alignment */
 #define APEX4_ERR_WORKSPACE 4    /* workspace smaller than apex4_gemm_workspace_size() */
 #define APEX4_ERR_HIP 5          /* the HIP runtime reported an error at launch */
