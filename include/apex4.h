@@ -201,8 +201,8 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
  * K); g = 256; per-channel (g = K).  Each mode's time is modelled as
  *     max(bytes / 5.0e12 B/s,  2*M*N*K / rate(mode)),
  * bytes = M*K/2 + N*K/2 + 4*(M*K/group_a + N*K/group_w) + 2*M*N, with
- * rate(mode) the GEMM rate measured on MI355X for that mode (g = 32: 485,
- * 64: 817, 128: 1565, mixed: 1672, 256: 1750, K: 2316 TOPS), and the finest
+ * rate(mode) the GEMM rate measured on MI355X for that mode (g = 32: 581,
+ * 64: 834, 128: 1565, mixed: 1672, 256: 1750, K: 2316 TOPS), and the finest
  * mode whose modelled speed is at least min_rel_speed times the fastest
  * mode's is returned.  Modes whose groups do not divide K are skipped.
  * Host function: touches no device memory.

@@ -15,7 +15,7 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound: 1565/2316 = 0.676 >= 0.65 > 817/2316 = 0.35
+    # compute-bound: 1565/2316 = 0.676 >= 0.65 > 834/2316 = 0.36
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 

@@ -30,17 +30,18 @@
 // fetched into registers (16-byte global loads) while the current one is
 // multiplied.
 //
-// Group rescale, equal group sizes >= 128.  The products S = s_a[m]*s_w[n] of
+// Group rescale, equal group sizes.  The products S = s_a[m]*s_w[n] of
 // a 32x32 tile come from one v_mfma_f32_32x32x16_bf16 instead of 16 vector
 // multiplies per lane: each scale is split exactly into three bf16 pieces
 // s = x0 + x1 + x2 (8 significant bits each, truncation), and the six largest
 // cross products x_p*y_q (p+q <= 2) fill six of the 16 K slots; the three
 // dropped ones are below 2^-23 of S.  The pieces are formed once per
 // workgroup by the threads that stage the scales, and stored in LDS in the
-// operand layout.  The vector work left per output and group is one int->fp32
-// conversion and one fma.  Smaller groups (32, 64) use plain fp32 scale
-// tables and a vector multiply; mixed mode (per-channel weights) needs no
-// product and applies s_w once in the epilogue.
+// operand layout, one table per group of the stage (4 at g = 32, 2 at
+// g = 64).  The vector work left per output and group is one int->fp32
+// conversion and one fma.  Mixed mode (per-channel weights) needs no product:
+// it rescales with s_a from a plain fp32 table and applies s_w once in the
+// epilogue.
 //
 // Rescale cadence follows the group size gs = min(g_a, g_w): after every
 // K-step (gs = 32), every second step (64), or every gs/128 stages (>= 128).
@@ -111,11 +112,11 @@ __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane
 
 // GS_STEPS: K-steps (of 32) per group: 1 or 2 (groups of 32 or 64), 4 (one
 // group per stage, g = 128), or 0 when a group spans several stages.  SPLIT:
-// the scale product comes from the bf16 MFMA (equal group sizes >= 128).
+// the scale product comes from the bf16 MFMA (equal group sizes).
 template <int GS_STEPS, bool MIXED, bool DEBUG_P>
 __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
 {
-    constexpr bool SPLIT = !MIXED && (GS_STEPS == 0 || GS_STEPS == 4);
+    constexpr bool SPLIT = !MIXED;
     constexpr bool SMALL = GS_STEPS == 1 || GS_STEPS == 2;    // several groups per stage
     constexpr int SUBS = SMALL ? MAX_SUB / GS_STEPS : 1;       // scale groups per stage
     constexpr int NS = (BM * SUBS + THREADS - 1) / THREADS;    // scale values per thread per operand
@@ -124,13 +125,17 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
     // Scale tables, per stage buffer: fp32 scales [SUBS][BM] and [SUBS][BN]
     // (small groups, mixed mode), or for SPLIT the bf16 split operands, one
     // 16-byte row per tile row (the last dword always 0).
-    constexpr int TAB_A = SPLIT ? BM * 4 : SUBS * BM;                 // floats / dwords per buffer
-    constexpr int TAB_B = SPLIT ? BN * 4 : (MIXED ? 0 : SUBS * BN);
+    constexpr int TAB_A = SUBS * BM * (SPLIT ? 4 : 1);                // floats / dwords per buffer
+    constexpr int TAB_B = MIXED ? 0 : SUBS * BN * (SPLIT ? 4 : 1);
     __shared__ __attribute__((aligned(16))) float lds_tab[2 * (TAB_A + TAB_B)];
     auto sa_tab = [&](int buf, int sub) -> float* { return lds_tab + buf * TAB_A + sub * BM; };
     auto sw_tab = [&](int buf, int sub) -> float* { return lds_tab + 2 * TAB_A + buf * TAB_B + sub * BN; };
-    auto spa_tab = [&](int buf) -> uint4* { return reinterpret_cast<uint4*>(lds_tab + buf * TAB_A); };
-    auto spb_tab = [&](int buf) -> uint4* { return reinterpret_cast<uint4*>(lds_tab + 2 * TAB_A + buf * TAB_B); };
+    auto spa_tab = [&](int buf, int sub) -> uint4* {
+        return reinterpret_cast<uint4*>(lds_tab + buf * TAB_A + sub * BM * 4);
+    };
+    auto spb_tab = [&](int buf, int sub) -> uint4* {
+        return reinterpret_cast<uint4*>(lds_tab + 2 * TAB_A + buf * TAB_B + sub * BN * 4);
+    };
     // A zero row for lanes 32..63 of the split-operand MFMA (their K slots
     // 8..15 are unused): the padding of row 0 of A buffer 0, which no stage
     // ever writes.
@@ -210,17 +215,24 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
             *reinterpret_cast<uint4*>(&lds_b[buf][o + 16]) = widen_hi(rb[set][i]);
         }
         if constexpr (SPLIT) {
-            // bf16 split operands: A row (slots 0..5) x0 x0 x0 x1 x1 x2,
-            // B row y0 y1 y2 y0 y1 y0, so slot k holds x_p*y_q with p+q <= 2
-            if (tid < BM) {
-                uint32_t x0, x1, x2;
-                split3(rsa[set][0], x0, x1, x2);
-                spa_tab(buf)[tid] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
-            }
-            if (tid < BN) {
-                uint32_t y0, y1, y2;
-                split3(rsw[set][0], y0, y1, y2);
-                spb_tab(buf)[tid] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+            // bf16 split operands of each of the stage's SUBS groups: A row
+            // (slots 0..5) x0 x0 x0 x1 x1 x2, B row y0 y1 y2 y0 y1 y0, so
+            // slot k holds x_p*y_q with p+q <= 2
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int idx = tid + THREADS * i;
+                const int row = idx & (BM - 1), sub = idx / BM;
+                if (sub < SUBS) {
+                    uint32_t x0, x1, x2;
+                    split3(rsa[set][i], x0, x1, x2);
+                    spa_tab(buf, sub)[row] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
+                }
+                const int rowb = idx & (BN - 1), subb = idx / BN;
+                if (subb < SUBS) {
+                    uint32_t y0, y1, y2;
+                    split3(rsw[set][i], y0, y1, y2);
+                    spb_tab(buf, subb)[rowb] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+                }
             }
         } else {
 #pragma unroll
@@ -256,16 +268,16 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
     // bf16 split operands of this wave's rows and columns (lanes 32..63 read
     // the zero row: their K slots 8..15 are unused)
     v8bf opa[2], opb[2];
-    auto load_split_operands = [&](int buf) {
+    auto load_split_operands = [&](int buf, int sub) {
         if constexpr (SPLIT) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const uint4* p = (lane < 32) ? &spa_tab(buf)[wm * 64 + mt * 32 + lane] : lds_zero;
+                const uint4* p = (lane < 32) ? &spa_tab(buf, sub)[wm * 64 + mt * 32 + lane] : lds_zero;
                 opa[mt] = __builtin_bit_cast(v8bf, *p);
             }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const uint4* p = (lane < 32) ? &spb_tab(buf)[wn * 64 + nt * 32 + lane] : lds_zero;
+                const uint4* p = (lane < 32) ? &spb_tab(buf, sub)[wn * 64 + nt * 32 + lane] : lds_zero;
                 opb[nt] = __builtin_bit_cast(v8bf, *p);
             }
         }
@@ -276,8 +288,8 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
     // stage buffer `buf`.
     auto tile_scales = [&](int buf, int mt, int nt) -> v16f {
         if constexpr (SPLIT) {
-            const uint4* pa = (lane < 32) ? &spa_tab(buf)[wm * 64 + mt * 32 + lane] : lds_zero;
-            const uint4* pb = (lane < 32) ? &spb_tab(buf)[wn * 64 + nt * 32 + lane] : lds_zero;
+            const uint4* pa = (lane < 32) ? &spa_tab(buf, 0)[wm * 64 + mt * 32 + lane] : lds_zero;
+            const uint4* pb = (lane < 32) ? &spb_tab(buf, 0)[wn * 64 + nt * 32 + lane] : lds_zero;
             return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, *pa),
                                                            __builtin_bit_cast(v8bf, *pb), v16f{}, 0, 0, 0);
         } else {
@@ -355,7 +367,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
     };
     auto rescale_tile = [&](int buf, int mt, int nt, int j) { rescale_tile_sub(buf, 0, mt, nt, j); };
     auto rescale_all = [&](int buf, int sub, int j) {
-        if constexpr (SPLIT) load_split_operands(buf);
+        if constexpr (SPLIT) load_split_operands(buf, sub);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll

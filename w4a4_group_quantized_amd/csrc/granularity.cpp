@@ -22,11 +22,11 @@ struct Mode {
 // Finest to coarsest: activation groups first (the activations carry the
 // outliers), then weight groups.  Rates: bench.py --workload sweep-*, GEMM
 // alone (roofline.achieved), Student-t activations, all six on one GPU
-// (g = 256 re-measured after a kernel change and scaled to that GPU by the
-// g = 128 rate measured beside it).
+// (g = 32, 64 and 256 re-measured after kernel changes; g = 256 scaled to
+// that GPU by the g = 128 rate measured beside it).
 constexpr Mode kModes[] = {
-    {32, 32, 485e12},
-    {64, 64, 817e12},
+    {32, 32, 581e12},
+    {64, 64, 834e12},
     {128, 128, 1565e12},
     {128, 0, 1672e12},    // mixed: per-channel weights, activation groups of 128
     {256, 256, 1750e12},
