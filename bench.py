@@ -8,19 +8,23 @@ for every layer of the workload, online activation quantization
 (apex4_gemm_w4a4), on weights packed once beforehand (untimed, as weights are
 packed offline).  Inputs sit in HBM before the timed region starts.
 
-The default workload is the LLaMA-2-7B-shaped prefill layer set at M=2048
-tokens with g=128: fused QKV (K=4096, N=12288), O-proj (4096, 4096),
-gate+up (4096, 22016) and down (11008, 4096); activations N(0,1) with 1% fixed
-outlier channels x20, weights N(0, 0.02).  Other workloads (decode, 70B
-prefill, the granularity sweep) are selectable for measurement runs.
+The default workload is the LLaMA-2-70B-shaped prefill layer set at M=4096
+tokens with g=128 (the largest compute-bound set of the W4A4-g128 metric):
+GQA QKV (K=8192, N=10240), O-proj (8192, 8192), gate+up (8192, 57344) and
+down (28672, 8192); activations N(0,1) with 1% fixed outlier channels x20,
+weights N(0, 0.02).  Other workloads (7B prefill, decode, the granularity
+sweep) are selectable for measurement runs.
 
 Prints ONE JSON line: value = effective TOPS (sum of 2*M*N*K over the step's
 GEMMs / step time), plus a roofline object for the GEMM kernel (int8 MFMA
 peak, or HBM for memory-bound workloads) and the CPU oracle timed on a
 bounded row sample.  The timed steps launch eagerly (--graph: replay one
 captured HIP graph per step).  The roofline's kernel duration comes from HIP
-events around back-to-back GEMM launches of each layer on the launch stream,
-so no host gap is counted in it.
+events on the launch stream: for compute-bound workloads a pair around every
+GEMM launch inside the timed steps (the GEMM as the metric sees it, right
+after its activation quantization), for memory-bound ones (where an event
+pair would weigh on a step of a few tens of microseconds) around back-to-back
+launches of each layer cycling the weight copies; both figures are reported.
 """
 from __future__ import annotations
 
@@ -87,7 +91,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama2-7b-prefill",
+    ap.add_argument("--workload", default="llama2-70b-prefill",
                     choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS) + sorted(F8_WORKLOADS)
                     + sorted(FUSED_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -344,8 +348,10 @@ def measure_ceilings(torch, apex4):
     out = {"mfma_i8_TOPS": best(lambda: apex4.probe_mfma_i8(2000, isink)) / 1e12,
            "hbm_read_GBps": best(lambda: apex4.probe_hbm_read(buf, isink)) / 1e9,
            "valu_f32_TFLOPs": best(lambda: apex4.probe_valu_f32(4000, fsink)) / 1e12,
+           "lds_read_TBps": best(lambda: apex4.probe_lds_read(4000, isink)) / 1e12,
            "method": "apex4_probe_* kernels: 4096 waves of independent v_mfma_i32_32x32x32_i8; "
-                     "whole-4KB-row reads of 2 GiB; 8 fp32 FMA chains per thread (no packed fp32)"}
+                     "whole-4KB-row reads of 2 GiB; 8 fp32 FMA chains per thread (no packed fp32); "
+                     "conflict-free 16-byte LDS reads, 16 waves per CU"}
     del buf
     return out
 
@@ -423,13 +429,19 @@ def main():
     bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)
                   + (2 * M * K - M * K / 2 - 4 * M * K / ga if fused else 0) for (K, N) in layers]
 
-    def step(i):
-        for (K, N, tx, qa, sa, qw, sw, y) in sets[i % copies]:
+    launch = torch.cuda.current_stream()
+
+    def step(i, marks=None):
+        for li, (K, N, tx, qa, sa, qw, sw, y) in enumerate(sets[i % copies]):
             if fused:
                 linear(tx, qw, sw, y)
             else:
                 quant(tx, (qa, sa))
+                if marks is not None:
+                    marks[li][0].record(launch)
                 gemm(qa, sa, qw, sw, K, y)
+                if marks is not None:
+                    marks[li][1].record(launch)
 
     for i in range(args.warmup):
         step(i)
@@ -456,14 +468,29 @@ def main():
         else:
             graphs[i % copies].replay()
 
-    # timed region: K steps, synchronized on both sides
+    # timed region: K steps, synchronized on both sides.  Compute-bound
+    # workloads (eager launches) carry an event pair around every GEMM: the
+    # kernel durations inside the steps, where each GEMM follows its
+    # activation quantization
+    in_step = bound == "mfma" and graphs is None and not fused
+    marks = None
+    if in_step:
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        marks = [[[ev(), ev()] for _ in layers] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run(s)
+        if in_step:
+            step(s, marks[s])
+        else:
+            run(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    gemm_ms_step = None
+    if in_step:
+        gemm_ms_step = np.array([[m[li][0].elapsed_time(m[li][1]) for li in range(len(layers))]
+                                 for m in marks]).mean(axis=0)
 
     # GEMM kernel duration per layer, for the roofline: R back-to-back
     # launches (cycling the weight copies) between two HIP events on the
@@ -471,7 +498,6 @@ def main():
     # ahead of the GPU, so no host gap sits inside the measured interval
     R = max(copies, 8)
     gemm_ms_avg = []
-    launch = torch.cuda.current_stream()
     for li, (K, N) in enumerate(layers):
         def gemms():
             for r in range(R):
@@ -497,7 +523,9 @@ def main():
         e1.record(launch)
         torch.cuda.synchronize()
         gemm_ms_avg.append(e0.elapsed_time(e1) / (reps * R))
-    gemm_ms_avg = np.array(gemm_ms_avg)
+    gemm_ms_b2b = np.array(gemm_ms_avg)
+    # the roofline's kernel time: in the steps where measured there
+    gemm_ms_avg = gemm_ms_step if gemm_ms_step is not None else gemm_ms_b2b
     layer_ops = np.array([rl.gemm_ops(M, N, K) for (K, N) in layers])
     if bound == "mfma":
         achieved = float(layer_ops.sum() / (gemm_ms_avg.sum() * 1e-3)) / 1e12
@@ -509,9 +537,10 @@ def main():
         unit = "GB/s"
 
     per_layer = [{"K": K, "N": N, "gemm_us": round(float(t) * 1e3, 2),
+                  "gemm_b2b_us": round(float(tb) * 1e3, 2),
                   "gemm_tops": round(float(o / (t * 1e-3)) / 1e12, 1),
                   "gemm_hbm_gbs": round(float(b / (t * 1e-3)) / 1e9, 1)}
-                 for (K, N), t, o, b in zip(layers, gemm_ms_avg, layer_ops, bytes_gemm)]
+                 for (K, N), t, tb, o, b in zip(layers, gemm_ms_avg, gemm_ms_b2b, layer_ops, bytes_gemm)]
     print(json.dumps({"workload": args.workload, "per_layer": per_layer}), file=sys.stderr)
 
     ceilings = None if args.no_ceilings else measure_ceilings(torch, apex4)
@@ -550,6 +579,10 @@ def main():
                      "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else
                      "fused quantize + gemm (apex4_linear_w4a4)" if fused else "gemm (apex4_gemm_w4a4)",
                      "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3),
+                     "kernel_timing": "event pair around every GEMM launch in the timed steps" if in_step
+                     else "events around back-to-back launches per layer (weight copies cycled)",
+                     "kernel_b2b_avg_us": float(gemm_ms_b2b.mean() * 1e3),
+                     "per_layer_us": [round(float(t) * 1e3, 2) for t in gemm_ms_avg],
                      "measured_ceiling": measured,
                      "frac_of_measured": None if measured is None else achieved / measured},
         "ceilings": ceilings,

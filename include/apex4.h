@@ -121,13 +121,35 @@ size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
  *   group_a in {32, 64, 128, 256} or group_a == K, and either
  *   group_w == group_a, or group_w == K (mixed granularity: per-channel
  *   weights, grouped activations).  M, N, K < 2^31 and M*N*G < 2^31 when
- *   psum_dbg is given.
+ *   psum_dbg is given.  One group over all of K (group_a == group_w == K)
+ *   needs K < 2^17 = 131072: the group's integer sum is held in one int32
+ *   register as 256 times its value (the codes enter the int8 matrix
+ *   instruction as 16 c), and 256 * 64 * K must stay below 2^31.  Larger K
+ *   with one group returns APEX4_ERR_UNSUPPORTED (groups of at most 256, or
+ *   mixed mode, have no such limit).
  */
 apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_a,
                              const void* qw_u8, const float* s_w, int32_t group_w,
                              int64_t M, int64_t N, int64_t K,
                              void* y_f16, float* y_f32, int32_t* psum_dbg,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * apex4_gemm_w4a4 with the per-group sums of selected rows only, for checking
+ * large shapes in the launch configuration apex4_gemm_w4a4 uses (debug; slow).
+ * Output row m = p_row0 + i * p_step (i < p_rows) has its sums P_j[m, n] in
+ * psum_dbg[i, n, j] (int32 [p_rows, N, G]); no other row's sums are written.
+ * Y, y_f32 and every other argument are exactly those of apex4_gemm_w4a4,
+ * whose psum_dbg is this call with p_row0 = 0, p_step = 1, p_rows = M.
+ *   p_row0 >= 0, p_step >= 1, p_rows >= 0 (0: no sums, psum_dbg may be NULL),
+ *   p_row0 + (p_rows - 1) * p_step < M, p_rows * N * G < 2^31;
+ *   otherwise APEX4_ERR_INVALID_ARG, found on the host before any launch.
+ */
+apex4_status apex4_gemm_w4a4_debug(const void* qa_u8, const float* s_a, int32_t group_a,
+                                   const void* qw_u8, const float* s_w, int32_t group_w,
+                                   int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                   int64_t p_row0, int64_t p_step, int64_t p_rows, int32_t* psum_dbg,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One W4A4 linear layer call: Y = X * W^T with X quantized on the fly, i.e.

@@ -1,8 +1,8 @@
 /*
- * apex4_probe.h -- measurement probes of libapex4.so: three kernels that
+ * apex4_probe.h -- measurement probes of libapex4.so: four kernels that
  * measure, on the GPU at hand, the ceilings the W4A4 GEMM kernels are held
  * against (the int8 matrix-unit rate, the HBM read rate, the fp32 vector-ALU
- * rate), so that a result can be quoted against the chip's measured ceiling
+ * rate, the LDS read rate), so that a result can be quoted against the chip's measured ceiling
  * as well as its datasheet peak.  The APEX4 page (aiqbench news page,
  * Abstract) frames the method by the balance of the matrix (Tensor Core) and
  * vector (CUDA Core) throughputs of a GPU; these probes measure that balance
@@ -57,6 +57,18 @@ apex4_status apex4_probe_hbm_read(const void* buf, int64_t bytes, int32_t* sink,
  *              (1024 * 256 * iters * 8 * 2).
  */
 apex4_status apex4_probe_valu_f32(int64_t iters, float* sink, double* flops_out, void* stream);
+
+/*
+ * 16-byte LDS reads (ds_read_b128): 1024 workgroups of 4 waves, each with a
+ * 16 KB LDS buffer, every wave reading `iters` rounds of 8 independent
+ * 1 KB pieces (lane l at byte 16 l of a piece: no bank conflicts).  The LDS
+ * bytes a compute unit can deliver per clock bound how many operand bytes a
+ * GEMM can feed its matrix instructions from LDS.
+ *   iters: 1 .. 2^30.   sink: device int32[1], 4-byte aligned.
+ *   bytes_out: HOST double, set to the LDS bytes read
+ *              (1024 * 256 * iters * 8 * 16).
+ */
+apex4_status apex4_probe_lds_read(int64_t iters, int32_t* sink, double* bytes_out, void* stream);
 
 #ifdef __cplusplus
 }

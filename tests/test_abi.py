@@ -161,7 +161,105 @@ def test_probe_validation(L):
     assert L.apex4_probe_mfma_i8(10, MIS, ctypes.byref(d), None) == ALIGN
     assert L.apex4_probe_valu_f32(0, A16, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_valu_f32(10, A16, None, None) == INVALID
+    assert L.apex4_probe_lds_read(0, A16, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_lds_read(1 << 31, A16, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_lds_read(10, MIS, ctypes.byref(d), None) == ALIGN
     assert L.apex4_probe_hbm_read(A16, 4095, A16b, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_hbm_read(A16, 0, A16b, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_hbm_read(None, 4096, A16b, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_hbm_read(MIS, 4096, A16b, ctypes.byref(d), None) == ALIGN
+
+
+def test_per_channel_int32_limit(L):
+    """One group over all of K keeps 256 * P in one int32: K < 2^17.  The
+    refusal comes before the pointer checks, so a NULL y16 tells the two
+    apart: UNSUPPORTED at K = 2^17, the next check (INVALID) just below."""
+    big, ok = 1 << 17, (1 << 17) - 128
+    assert _gemm(L, ga=big, gw=big, K=big) == UNSUPPORTED
+    assert _gemm(L, ga=ok, gw=ok, K=ok, y16=None) == INVALID
+    # groups of 128 and mixed mode sum at most one group of 128 per int32
+    assert _gemm(L, ga=128, gw=128, K=big, y16=None) == INVALID
+    assert _gemm(L, ga=128, gw=big, K=big, y16=None) == INVALID
+    assert _linear(L, ga=big, gw=big, K=big) == UNSUPPORTED
+    assert _linear(L, ga=ok, gw=ok, K=ok) == WORKSPACE      # (its next check: the codes need a workspace)
+    assert L.apex4_gemm_workspace_size(4096, 4096, big, big, big) == 0
+    assert L.apex4_linear_workspace_size(4096, 4096, big, big, big) == 0
+
+
+def _gemm_dbg(L, M=16, N=16, K=1024, ga=128, row0=0, step=1, rows=16, ps=A16b, y16=A16b):
+    return L.apex4_gemm_w4a4_debug(A16, A16b, ga, A16, A16b, ga, M, N, K, y16, None, row0, step, rows, ps,
+                                   None, 0, None)
+
+
+def test_gemm_debug_rows_validation(L):
+    """apex4_gemm_w4a4_debug: the kept rows must lie inside Y and their sums fit
+    32-bit indexing; otherwise INVALID before anything is launched.  (Valid
+    row selections pass on to the next check: a NULL y16 gives INVALID there
+    too, so those are told apart by the other arguments being valid.)"""
+    assert _gemm_dbg(L, step=0) == INVALID
+    assert _gemm_dbg(L, row0=-1) == INVALID
+    assert _gemm_dbg(L, rows=-1) == INVALID
+    assert _gemm_dbg(L, row0=15, step=1, rows=2) == INVALID          # row 16 of 16
+    assert _gemm_dbg(L, M=300, row0=44, step=256, rows=2) == INVALID  # row 300 of 300
+    assert _gemm_dbg(L, ps=None) == INVALID                           # sums asked, no buffer
+    assert _gemm_dbg(L, M=1 << 20, N=1 << 20, rows=4096, step=256) == INVALID   # 2^32 sums
+    assert _gemm_dbg(L, ps=A16b + 2) == ALIGN
+    # the same call with every argument valid but y16 is stopped at y16
+    assert _gemm_dbg(L, M=300, row0=43, step=256, rows=2, y16=None) == INVALID
+    # no rows kept: no sums buffer needed; empty shapes stay no-ops
+    assert _gemm_dbg(L, rows=0, ps=None, y16=A16b + 1) == ALIGN
+    assert L.apex4_gemm_w4a4_debug(None, None, 128, A16, A16b, 128, 0, 16, 1024, None, None, 0, 1, 0, None,
+                                   None, 0, None) == OK
+
+
+class _FakeGpuTensor:
+    """Just enough of a torch tensor for the binding's argument checks (which
+    run before anything is allocated or launched)."""
+
+    def __init__(self, shape, dtype, contiguous=True, device="cuda:0"):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self._contig = contiguous
+        self.device = torch.device(device)
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return self._contig
+
+
+def test_binding_refuses_mismatched_tensors():
+    """apex4.gemm / quantize_act check shapes, dtypes, contiguity and device
+    against (M, N, K, groups) before calling the library: a mismatch would
+    otherwise make a kernel read or write out of bounds."""
+    torch = pytest.importorskip("torch")
+    T = _FakeGpuTensor
+    M, N, K = 8, 16, 256
+    qa, sa = T((M, K // 2), torch.uint8), T((M, K // 128), torch.float32)
+    qw, sw = T((N, K // 2), torch.uint8), T((N, K // 128), torch.float32)
+    bad = [
+        dict(qa=T((M, K // 4), torch.uint8)),                       # K/2 columns expected
+        dict(sa=T((M, K // 64), torch.float32)),                    # K/ga scale columns
+        dict(sw=T((N + 1, K // 128), torch.float32)),               # N rows
+        dict(sa=T((M, K // 128), torch.float16)),                   # fp32 scales
+        dict(qw=T((N, K // 2), torch.uint8, contiguous=False)),
+        dict(qw=T((N, K // 2), torch.uint8, device="cuda:1")),      # another device
+        dict(y16=T((M, N - 1), torch.float16)),
+        dict(y16=T((M, N), torch.float16, contiguous=False)),
+        dict(y32=T((M, N), torch.float16)),
+    ]
+    for b in bad:
+        args = dict(qa=qa, sa=sa, qw=qw, sw=sw, y16=None, y32=None)
+        args.update(b)
+        with pytest.raises(ValueError):
+            apex4.gemm(args["qa"], args["sa"], 128, args["qw"], args["sw"], 128, K,
+                       y16=args["y16"], y32=args["y32"])
+    # an explicit K that disagrees with the codes
+    with pytest.raises(ValueError):
+        apex4.gemm(qa, sa, 128, qw, sw, 128, 2 * K)
+    # quantize_act into caller buffers of the wrong shape
+    x = T((M, K), torch.float16)
+    with pytest.raises(ValueError):
+        apex4.quantize_act(x, 128, out=(T((M, K // 2), torch.uint8), T((M, 1), torch.float32)))
+    with pytest.raises(ValueError):
+        apex4.quantize_act(x, 128, out=(T((M, K), torch.uint8), T((M, K // 128), torch.float32)))

@@ -105,13 +105,17 @@ def test_gemm_f8_matches_oracle(dev, M, N, K):
 
 @pytest.mark.gpu
 def test_gemm_f8_equals_int4_path(dev):
-    x, w = inputs.problem(300, 520, 2048, seed=5, act="student_t")
-    tx, tw, y32 = run_f8(dev, x, w)
+    # a whole number of rounds of 256x128 tiles (512 x 64 CUs columns), so the
+    # INT4 path runs over all of K in every tile, with no K split, and both
+    # add the groups in the same order
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    x, w = inputs.problem(512, 64 * cus, 2048, seed=5, act="student_t")
+    rows = np.array([0, 1, 255, 256, 300, 511])
+    tx, tw, y32 = run_f8(dev, x, w, rows=rows)
     qa, sa = apex4.quantize_act(tx, 128)
     qw, sw = apex4.pack_weight(tw, 128)
-    # (with the debug sums the INT4 path runs over all of K in every tile,
-    # no K split, so both add the groups in the same order)
-    _, y32i, _ = apex4.gemm(qa, sa, 128, qw, sw, 128, 2048, want_y32=True, want_psum=True)
+    assert apex4.workspace_size(512, 64 * cus, 2048, 128, 128) == 0
+    _, y32i, _ = apex4.gemm(qa, sa, 128, qw, sw, 128, 2048, want_y32=True)
     torch.cuda.synchronize()
     assert torch.equal(y32.view(torch.int32), y32i.view(torch.int32))
 

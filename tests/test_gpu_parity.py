@@ -59,8 +59,15 @@ def gpu_quantize(x, g, dev, weight=False):
     return q, s
 
 
-def run_case(dev, x, w, ga, gw, rows=None, want_p=False):
-    """Quantize X and pack W on the GPU, run the GEMM, compare everything."""
+def run_case(dev, x, w, ga, gw, rows=None, want_p=False, p_rows=None):
+    """Quantize X and pack W on the GPU, run the GEMM, compare everything.
+
+    rows: the output rows compared (None: all).  want_p: the per-group int32
+    sums are compared bit for bit, on `rows` (the GPU writes them for every
+    row), or, with p_rows = (row0, step, count), on rows row0 + i * step
+    only, which is all the GPU writes (apex4_gemm_w4a4_debug, in the launch
+    configuration of apex4_gemm_w4a4); those rows are compared for Y too.
+    """
     M, K = x.shape
     tqa, tsa = gpu_quantize(x, ga, dev)
     tqw, tsw = gpu_quantize(w, gw, dev, weight=True)
@@ -70,14 +77,29 @@ def run_case(dev, x, w, ga, gw, rows=None, want_p=False):
     assert np.array_equal(tsa.cpu().numpy().view(np.uint32), osa.view(np.uint32))
     assert np.array_equal(tqw.cpu().numpy(), oqw)
     assert np.array_equal(tsw.cpu().numpy().view(np.uint32), osw.view(np.uint32))
-    y16, y32, ps = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True, want_psum=want_p)
+    y16, y32, ps = apex4.gemm(tqa, tsa, ga, tqw, tsw, gw, K, want_y32=True, want_psum=want_p,
+                              psum_rows=p_rows)
     torch.cuda.synchronize()
-    r = np.arange(M) if rows is None else rows
+    r = np.arange(M) if rows is None else np.asarray(rows)
+    prow = None
+    if p_rows is not None:
+        row0, step, count = p_rows
+        prow = row0 + step * np.arange(count)
+        r = np.unique(np.concatenate([r, prow]))
     o16, o32, op = orc.gemm(oqa[r], osa[r], ga, oqw, osw, gw, K, want_p=want_p)
     rel = check_y(y32.cpu().numpy()[r], y16.cpu().numpy()[r], o32)
     if want_p:
-        assert np.array_equal(ps.cpu().numpy()[r], op)
+        gp = ps.cpu().numpy()
+        if prow is None:
+            assert np.array_equal(gp[r], op)
+        else:
+            assert np.array_equal(gp, op[np.searchsorted(r, prow)])
     return rel
+
+
+def tile_rows(M, row0):
+    """(row0, 256, count): one row in every 256-row tile of the tiled kernels."""
+    return (row0, 256, (M - 1 - row0) // 256 + 1)
 
 
 @functools.lru_cache(maxsize=1)
@@ -209,6 +231,23 @@ def test_gemm_decode_many_blocks(dev, M, N, K, ga, gw):
     run_case(dev, x, w, ga, gw, want_p=True)
 
 
+@pytest.mark.parametrize("M,g", [(1, 128), (2, 256), (8, 128), (13, "K"), (40, 128), (40, 256), (64, "K"),
+                                 (300, 128), (300, 256), (300, "K"), (300, 32), (520, 64)])
+def test_gemm_debug_rows(dev, M, g):
+    """apex4_gemm_w4a4_debug keeps the group sums of every p_step-th row from
+    p_row0: each kernel (row-streaming, LDS-streaming, K-outer, skinny,
+    ping-pong, step-major tiled) against the oracle.  The buffer is exactly
+    [count, N, G], so a sum of any other row written into it would overwrite
+    a kept row's entry and show as a mismatch."""
+    K = 1024
+    g = K if g == "K" else g
+    x, w = inputs.problem(M, 200, K, seed=5 + M, act="outlier")
+    row0 = M // 3
+    step = max(1, M // 5)
+    count = (M - 1 - row0) // step + 1
+    run_case(dev, x, w, g, g, rows=sample_rows(M, n=4), want_p=True, p_rows=(row0, step, count))
+
+
 @pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
 def test_gemm_unit_scales_integer_exact(dev, g):
     """Random packed codes (-8 included), all scales 1: Y is the exact integer matmul."""
@@ -268,30 +307,36 @@ PREFILL_70B = [(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)]
 DECODE = [(8192, 28672), (28672, 8192)]
 
 
+# Full sizes: Y on 16 sampled rows plus one row in every 256-row tile, whose
+# per-group int32 sums are compared too (the debug sums of those rows only,
+# from the same launch configuration as the plain call); decode shapes
+# compare every row and every sum.
+
+
 @pytest.mark.parametrize("K,N", PREFILL_7B)
 def test_full_7b_prefill(dev, K, N):
     x, w = big_problem(2048, N, K, "outlier")
-    run_case(dev, x, w, 128, 128, rows=sample_rows(2048))
+    run_case(dev, x, w, 128, 128, rows=sample_rows(2048), want_p=True, p_rows=tile_rows(2048, 101))
 
 
 @pytest.mark.parametrize("K,N", DECODE)
 @pytest.mark.parametrize("M", [1, 4, 16, 64])
 def test_full_decode(dev, M, K, N):
     x, w = big_problem(M, N, K, "normal")
-    run_case(dev, x, w, 128, 128, rows=None if M <= 16 else sample_rows(M))
+    run_case(dev, x, w, 128, 128, want_p=True)
 
 
 @pytest.mark.parametrize("K,N", PREFILL_70B)
 def test_full_70b_prefill(dev, K, N):
     x, w = big_problem(4096, N, K, "outlier")
-    run_case(dev, x, w, 128, 128, rows=sample_rows(4096, n=8))
+    run_case(dev, x, w, 128, 128, rows=sample_rows(4096), want_p=True, p_rows=tile_rows(4096, 190))
 
 
 @pytest.mark.parametrize("ga,gw", [(32, 32), (64, 64), (128, 128), (256, 256), (8192, 8192),
                                    (128, 8192)])
 def test_full_granularity_sweep(dev, ga, gw):
     x, w = big_problem(8192, 28672, 8192, "student_t")
-    run_case(dev, x, w, ga, gw, rows=sample_rows(8192, n=8))
+    run_case(dev, x, w, ga, gw, rows=sample_rows(8192), want_p=True, p_rows=tile_rows(8192, 37))
 
 
 # ------------------------------------------------- K split of a partial last round
@@ -319,7 +364,8 @@ def test_gemm_split_last_round(dev, M, N, K, ga, gw):
     else:
         assert ws == 0
     rows = np.unique(np.concatenate([sample_rows(M, n=8), np.arange(M - 3, M), np.arange(256, min(M, 259))]))
-    run_case(dev, x, w, ga, gw, rows=rows)
+    # the K parts write the group sums of their own groups
+    run_case(dev, x, w, ga, gw, rows=rows, want_p=True)
     # the parts are added in a fixed order: a second call gives the same bits
     tqa, tsa = gpu_quantize(x, ga, dev)
     tqw, tsw = gpu_quantize(w, gw, dev, weight=True)
@@ -357,7 +403,8 @@ def test_gemm_decode_split_k(dev, M, N, K, ga, gw):
     ws = apex4.workspace_size(M, N, K, ga, gw)
     assert ws == 2 * M * N * 4
     x, w = inputs.problem(M, N, K, seed=61 + M, act="outlier")
-    run_case(dev, x, w, ga, gw, rows=None if M <= 17 else sample_rows(M))
+    # (each half writes the group sums of its own groups)
+    run_case(dev, x, w, ga, gw, rows=None if M <= 17 else sample_rows(M), want_p=True)
     # the two halves are added in a fixed order: a second call gives the same bits
     tqa, tsa = gpu_quantize(x, ga, dev)
     tqw, tsw = gpu_quantize(w, gw, dev, weight=True)

@@ -51,3 +51,11 @@ def test_probe_valu(dev):
     flops, t = timed(lambda: apex4.probe_valu_f32(1000, sink))
     assert flops == 1024 * 256 * 1000 * 16
     assert 5e12 < flops / t < 400e12
+
+
+def test_probe_lds_read(dev):
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes, t = timed(lambda: apex4.probe_lds_read(2000, sink))
+    assert nbytes == 1024 * 256 * 2000 * 8 * 16
+    # 256 CUs x 128 or 256 bytes per clock at ~2 GHz: tens to ~160 TB/s
+    assert 5e12 < nbytes / t < 400e12

@@ -30,6 +30,8 @@ SIGNATURES = {
     "apex4_gemm_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_gemm_w4a4": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_gemm_w4a4_debug": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
+                                     _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "apex4_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_linear_w4a4": (_I32, [_P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
@@ -39,6 +41,7 @@ SIGNATURES = {
     "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_hbm_read": (_I32, [_P, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_valu_f32": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "apex4_probe_lds_read": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -76,13 +79,24 @@ def _stream(torch, device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need_gpu(t, name: str, dtype=None) -> None:
+def _need_gpu(t, name: str, dtype=None, shape=None, device=None) -> None:
+    """Refuse what the C ABI cannot check itself: a host tensor, a
+    non-contiguous one, the wrong dtype, the wrong shape or another device."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _cols(K: int, group: int) -> int:
+    """Scale columns K / group (0 for a group the library will refuse)."""
+    return K // group if group > 0 else 0
 
 
 def _ptr(t):
@@ -96,9 +110,11 @@ def quantize_act(x, group: int, out=None):
     M, K = x.shape
     if out is None:
         qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-        sa = torch.empty((M, K // group if group > 0 else 0), dtype=torch.float32, device=x.device)
+        sa = torch.empty((M, _cols(K, group)), dtype=torch.float32, device=x.device)
     else:
         qa, sa = out
+        _need_gpu(qa, "qa", torch.uint8, (M, K // 2), x.device)
+        _need_gpu(sa, "s_a", torch.float32, (M, _cols(K, group)), x.device)
     _check("apex4_quantize_act", lib().apex4_quantize_act(
         _ptr(x), M, K, group, _ptr(qa), _ptr(sa), _stream(torch, x.device)))
     return qa, sa
@@ -110,7 +126,7 @@ def pack_weight(w, group: int):
     _need_gpu(w, "w", torch.float16)
     N, K = w.shape
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-    sw = torch.empty((N, K // group if group > 0 else 0), dtype=torch.float32, device=w.device)
+    sw = torch.empty((N, _cols(K, group)), dtype=torch.float32, device=w.device)
     _check("apex4_pack_weight", lib().apex4_pack_weight(
         _ptr(w), N, K, group, _ptr(qw), _ptr(sw), _stream(torch, w.device)))
     return qw, sw
@@ -121,32 +137,47 @@ def workspace_size(M: int, N: int, K: int, ga: int, gw: int) -> int:
 
 
 def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bool = False,
-         want_psum: bool = False, y16=None, y32=None):
+         want_psum: bool = False, psum_rows: tuple | None = None, y16=None, y32=None):
     """Y = W4A4 GEMM with per-group dequantization (include/apex4.h).
 
     Returns y16 [M, N] fp16, or (y16, y32, psum) when want_y32/want_psum is set
-    (entries not asked for are None).
+    (entries not asked for are None).  psum_rows = (row0, step, count) keeps
+    the group sums of rows row0 + i * step only (apex4_gemm_w4a4_debug):
+    psum is then [count, N, G].
     """
     import torch
-    for t, n in ((qa, "qa"), (qw, "qw")):
-        _need_gpu(t, n, torch.uint8)
-    for t, n in ((sa, "s_a"), (sw, "s_w")):
-        _need_gpu(t, n, torch.float32)
     M, N = qa.shape[0], qw.shape[0]
     K = 2 * qa.shape[1] if K is None else K
     dev = qa.device
+    _need_gpu(qa, "qa", torch.uint8, (M, K // 2), dev)
+    _need_gpu(qw, "qw", torch.uint8, (N, K // 2), dev)
+    _need_gpu(sa, "s_a", torch.float32, (M, _cols(K, ga)), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, _cols(K, gw)), dev)
+    # caller buffers are checked before anything is allocated
+    if y16 is not None:
+        _need_gpu(y16, "y16", torch.float16, (M, N), dev)
+    if y32 is not None:
+        _need_gpu(y32, "y32", torch.float32, (M, N), dev)
     if y16 is None:
         y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
     if want_y32 and y32 is None:
         y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
     psum = None
+    G = _cols(K, min(ga, gw))
+    row0, step, count = psum_rows if psum_rows is not None else (0, 1, M)
     if want_psum:
-        psum = torch.empty((M, N, K // min(ga, gw)), dtype=torch.int32, device=dev)
+        psum = torch.empty((count, N, G), dtype=torch.int32, device=dev)
     ws_bytes = workspace_size(M, N, K, ga, gw)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    _check("apex4_gemm_w4a4", lib().apex4_gemm_w4a4(
-        _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K,
-        _ptr(y16), _ptr(y32), _ptr(psum), _ptr(ws), ws_bytes, _stream(torch, dev)))
+    if psum_rows is None:
+        _check("apex4_gemm_w4a4", lib().apex4_gemm_w4a4(
+            _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K,
+            _ptr(y16), _ptr(y32), _ptr(psum), _ptr(ws), ws_bytes, _stream(torch, dev)))
+    else:
+        _check("apex4_gemm_w4a4_debug", lib().apex4_gemm_w4a4_debug(
+            _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K,
+            _ptr(y16), _ptr(y32), row0, step, count if want_psum else 0, _ptr(psum),
+            _ptr(ws), ws_bytes, _stream(torch, dev)))
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16
@@ -163,11 +194,16 @@ def linear(x, ga: int, qw, sw, gw: int, *, want_y32: bool = False, y16=None, y32
     linear_workspace_size() bytes (allocated here when None)."""
     import torch
     _need_gpu(x, "x", torch.float16)
-    _need_gpu(qw, "qw", torch.uint8)
-    _need_gpu(sw, "s_w", torch.float32)
     M, K = x.shape
     N = qw.shape[0]
     dev = x.device
+    _need_gpu(qw, "qw", torch.uint8, (N, K // 2), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, _cols(K, gw)), dev)
+    # caller buffers are checked before anything is allocated
+    if y16 is not None:
+        _need_gpu(y16, "y16", torch.float16, (M, N), dev)
+    if y32 is not None:
+        _need_gpu(y32, "y32", torch.float32, (M, N), dev)
     if y16 is None:
         y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
     if want_y32 and y32 is None:
@@ -175,6 +211,8 @@ def linear(x, ga: int, qw, sw, gw: int, *, want_y32: bool = False, y16=None, y32
     need = linear_workspace_size(M, N, K, ga, gw)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need_gpu(workspace, "workspace", torch.uint8, None, dev)
     nbytes = 0 if workspace is None else workspace.numel()
     _check("apex4_linear_w4a4", lib().apex4_linear_w4a4(
         _ptr(x), ga, _ptr(qw), _ptr(sw), gw, M, N, K, _ptr(y16), _ptr(y32), _ptr(workspace), nbytes,
@@ -190,9 +228,11 @@ def quantize_f8(x, group: int = 128, out=None):
     rows, K = x.shape
     if out is None:
         q8 = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
-        s = torch.empty((rows, K // group if group > 0 else 0), dtype=torch.float32, device=x.device)
+        s = torch.empty((rows, _cols(K, group)), dtype=torch.float32, device=x.device)
     else:
         q8, s = out
+        _need_gpu(q8, "q8", torch.uint8, (rows, K), x.device)
+        _need_gpu(s, "s", torch.float32, (rows, _cols(K, group)), x.device)
     _check("apex4_quantize_f8", lib().apex4_quantize_f8(
         _ptr(x), rows, K, group, _ptr(q8), _ptr(s), _stream(torch, x.device)))
     return q8, s
@@ -202,13 +242,18 @@ def gemm_f8(qa8, sa, qw8, sw, *, want_y32: bool = False, want_psum: bool = False
     """apex4_gemm_w4a4_f8: the W4A4 GEMM (groups of 128) on E4M3-coded operands.
     Returns y16, or (y16, y32, psum) when want_y32/want_psum is set."""
     import torch
-    for t, n in ((qa8, "qa8"), (qw8, "qw8")):
-        _need_gpu(t, n, torch.uint8)
-    for t, n in ((sa, "s_a"), (sw, "s_w")):
-        _need_gpu(t, n, torch.float32)
     M, K = qa8.shape
     N = qw8.shape[0]
     dev = qa8.device
+    _need_gpu(qa8, "qa8", torch.uint8, (M, K), dev)
+    _need_gpu(qw8, "qw8", torch.uint8, (N, K), dev)
+    _need_gpu(sa, "s_a", torch.float32, (M, K // 128), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, K // 128), dev)
+    # caller buffers are checked before anything is allocated
+    if y16 is not None:
+        _need_gpu(y16, "y16", torch.float16, (M, N), dev)
+    if y32 is not None:
+        _need_gpu(y32, "y32", torch.float32, (M, N), dev)
     if y16 is None:
         y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
     if want_y32 and y32 is None:
@@ -258,3 +303,9 @@ def probe_valu_f32(iters: int, sink) -> float:
     """fp32 FMA chains on the vector ALU; returns the floating-point operations."""
     _need_gpu(sink, "sink")
     return _probe("apex4_probe_valu_f32", iters, _ptr(sink))
+
+
+def probe_lds_read(iters: int, sink) -> float:
+    """16-byte LDS reads, conflict-free; returns the LDS bytes read."""
+    _need_gpu(sink, "sink")
+    return _probe("apex4_probe_lds_read", iters, _ptr(sink))

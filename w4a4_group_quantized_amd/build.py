@@ -32,27 +32,31 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def _compile(src: str, bdir: str, defines: tuple, verbose: bool) -> str:
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *HIP_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; anything else is shown
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{msg}")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+        if msg.strip():
+            print(msg)
+    return obj
+
+
 def build(verbose: bool = False, out: str | None = None, defines: tuple = ()) -> str:
-    """Compile every source and link libapex4.so (or `out`, with extra -D defines)."""
-    objs = []
+    """Compile every source (in parallel) and link libapex4.so (or `out`, with extra -D defines)."""
+    from concurrent.futures import ThreadPoolExecutor
     lib = out or LIB
     bdir = os.path.join(os.path.dirname(lib), "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in sources():
-        obj = os.path.join(bdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *HIP_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC,
-               "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        # the host pass does not know the packed-fp32 feature and says so; anything else is shown
-        noise = "'-packed-fp32-ops' is not a recognized feature"
-        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{msg}")
-        if msg.strip() and verbose:
-            print(msg)
-        objs.append(obj)
+    jobs = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, bdir, defines, verbose), sources()))
     tmp = lib + ".tmp"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, lib)

@@ -30,6 +30,17 @@ apex4_status check_quantize(const void* x, int64_t rows, int64_t K, int32_t g, c
 
 apex4_status to_status(hipError_t e) { return e == hipSuccess ? APEX4_OK : APEX4_ERR_HIP; }
 
+// One group over all of K keeps the kernels' int32 group sum (of the codes
+// widened to 16 c, i.e. 256 times the sum) over the whole row: |256 P| <=
+// 256 * 64 * K must stay below 2^31, so K < 2^17 there.
+constexpr int64_t kMaxPerChannelK = int64_t(1) << 17;
+
+bool per_channel_overflows(int64_t K, int32_t group_a, int32_t group_w)
+{
+    return group_a == K && group_w == K && K >= kMaxPerChannelK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +85,7 @@ bool linear_problem(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t gr
 {
     if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0) return false;
     if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return false;
+    if (per_channel_overflows(K, group_a, group_w)) return false;
     p = apex4::GemmProblem{};
     p.M = static_cast<int32_t>(M);
     p.N = static_cast<int32_t>(N);
@@ -103,6 +115,7 @@ apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* q
     if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return APEX4_ERR_INVALID_ARG;
     if (!small_group(group_a) && group_a != K) return APEX4_ERR_UNSUPPORTED;
     if (!(group_w == group_a || group_w == K)) return APEX4_ERR_UNSUPPORTED;
+    if (per_channel_overflows(K, group_a, group_w)) return APEX4_ERR_UNSUPPORTED;
     const size_t need = apex4_linear_workspace_size(M, N, K, group_a, group_w);
     if (workspace_bytes < need || (need > 0 && !workspace)) return APEX4_ERR_WORKSPACE;
     if (M == 0 || N == 0) return APEX4_OK;
@@ -148,7 +161,8 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
 {
     if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
         return APEX4_ERR_INVALID_ARG;
-    if (psum_dbg && M * N * (K / 128) > kMaxDim) return APEX4_ERR_INVALID_ARG;
+    if (psum_dbg && (unsigned __int128)M * (uint64_t)N * (uint64_t)(K / 128) > (uint64_t)kMaxDim)
+        return APEX4_ERR_INVALID_ARG;
     // 32-bit offsets within a 256-row block of operand bytes
     if ((uint64_t)K * 256 >= (1ull << 31)) return APEX4_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return APEX4_OK;
@@ -169,6 +183,7 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
     p.y16 = y_f16;
     p.y32 = y_f32;
     p.psum = psum_dbg;
+    p.prows.count = static_cast<int32_t>(M);
     return to_status(apex4::launch_gemm_pingpong_f8(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -177,6 +192,7 @@ size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
     // shapes apex4_gemm_w4a4 rejects, or that launch nothing, need none
     if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0) return 0;
     if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0) return 0;
+    if (per_channel_overflows(K, group_a, group_w)) return 0;
     apex4::GemmProblem p{};
     p.M = static_cast<int32_t>(M);
     p.N = static_cast<int32_t>(N);
@@ -191,14 +207,44 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
                              int64_t N, int64_t K, void* y_f16, float* y_f32, int32_t* psum_dbg,
                              void* workspace, size_t workspace_bytes, void* stream)
 {
+    return apex4::gemm_checked(qa_u8, s_a, group_a, qw_u8, s_w, group_w, M, N, K, y_f16, y_f32, 0, 1, M, psum_dbg,
+                        workspace, workspace_bytes, stream);
+}
+
+apex4_status apex4_gemm_w4a4_debug(const void* qa_u8, const float* s_a, int32_t group_a,
+                                   const void* qw_u8, const float* s_w, int32_t group_w, int64_t M,
+                                   int64_t N, int64_t K, void* y_f16, float* y_f32, int64_t p_row0,
+                                   int64_t p_step, int64_t p_rows, int32_t* psum_dbg, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    if (p_row0 < 0 || p_step < 1 || p_rows < 0 || p_row0 > kMaxDim || p_step > kMaxDim || p_rows > kMaxDim)
+        return APEX4_ERR_INVALID_ARG;
+    // every kept row lies inside Y
+    if (M > 0 && p_rows > 0 && p_row0 + (p_rows - 1) * p_step >= M) return APEX4_ERR_INVALID_ARG;
+    if (p_rows > 0 && !psum_dbg) return APEX4_ERR_INVALID_ARG;
+    return apex4::gemm_checked(qa_u8, s_a, group_a, qw_u8, s_w, group_w, M, N, K, y_f16, y_f32, p_row0, p_step, p_rows,
+                        p_rows > 0 ? psum_dbg : nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace apex4 {
+
+apex4_status gemm_checked(const void* qa_u8, const float* s_a, int32_t group_a, const void* qw_u8,
+                          const float* s_w, int32_t group_w, int64_t M, int64_t N, int64_t K, void* y_f16,
+                          float* y_f32, int64_t p_row0, int64_t p_step, int64_t p_rows, int32_t* psum_dbg,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
     if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
         return APEX4_ERR_INVALID_ARG;
     if (group_a <= 0 || group_w <= 0 || K % group_a != 0 || K % group_w != 0)
         return APEX4_ERR_INVALID_ARG;
     if (!small_group(group_a) && group_a != K) return APEX4_ERR_UNSUPPORTED;
     if (!(group_w == group_a || group_w == K)) return APEX4_ERR_UNSUPPORTED;
+    if (per_channel_overflows(K, group_a, group_w)) return APEX4_ERR_UNSUPPORTED;
     const int64_t gs = group_a < group_w ? group_a : group_w;
-    if (psum_dbg && M * N * (K / gs) > kMaxDim) return APEX4_ERR_INVALID_ARG;
+    if (psum_dbg && (unsigned __int128)p_rows * (uint64_t)N * (uint64_t)(K / gs) > (uint64_t)kMaxDim)
+        return APEX4_ERR_INVALID_ARG;
     const size_t need = apex4_gemm_workspace_size(M, N, K, group_a, group_w);
     if (workspace_bytes < need || (need > 0 && !workspace)) return APEX4_ERR_WORKSPACE;
     if (M == 0 || N == 0) return APEX4_OK;
@@ -207,7 +253,7 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
         !aligned(y_f16, 2) || !aligned(y_f32, 4) || !aligned(psum_dbg, 4) || !aligned(workspace, 16))
         return APEX4_ERR_ALIGNMENT;
 
-    apex4::GemmProblem p;
+    apex4::GemmProblem p{};
     p.qa = static_cast<const uint8_t*>(qa_u8);
     p.sa = s_a;
     p.qw = static_cast<const uint8_t*>(qw_u8);
@@ -220,9 +266,13 @@ apex4_status apex4_gemm_w4a4(const void* qa_u8, const float* s_a, int32_t group_
     p.y16 = y_f16;
     p.y32 = y_f32;
     p.psum = psum_dbg;
+    p.prows.row0 = static_cast<int32_t>(p_row0);
+    p.prows.step = static_cast<int32_t>(p_step);
+    p.prows.count = static_cast<int32_t>(p_rows);
     p.ws = workspace;
     p.ws_bytes = workspace_bytes;
     return to_status(apex4::launch_gemm(p, static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
+}  // namespace apex4
+

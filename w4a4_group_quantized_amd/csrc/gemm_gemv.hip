@@ -61,6 +61,7 @@ struct GemvArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes)
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
                 const float S = MIXED ? sa : sa * ws[k];
                 acc[m] = fmaf(S, (float)P, acc[m]);
                 if (DEBUG_P && owner && m < a.M)
-                    a.psum[((int64_t)m * a.N + n) * a.G + (GM == 2 ? (u >> 1) : u)] = P;
+                    if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, a.G, GM == 2 ? (u >> 1) : u)) *d = P;
             }
         }
         if (p == passes - 1) {
@@ -231,7 +232,8 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
                     const int Pt = wave_sum_int(pint[m]);
                     const float S = lsa[m * a.Ga] * ws[k];
                     v = S * (float)Pt;
-                    if (DEBUG_P && lane == 0 && m < a.M) a.psum[(int64_t)m * a.N + n] = Pt;
+                    if (DEBUG_P && lane == 0 && m < a.M)
+                        if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, 1, 0)) *d = Pt;
                     pint[m] = 0;
                 } else {
                     v = wave_sum(acc[m]);
@@ -371,6 +373,7 @@ hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream)
     g.y16 = static_cast<_Float16*>(p.y16);
     g.y32 = p.y32;
     g.psum = p.psum;
+    g.prows = p.prows;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     const int gm = gs == p.K && !mixed ? 0 : gs == 2 * UNIT ? 2 : 1;
     const bool dbg = p.psum != nullptr;

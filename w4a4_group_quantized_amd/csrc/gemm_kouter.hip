@@ -75,6 +75,7 @@ struct KouterArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
     // K split (groups of 128): the workgroups come in kparts equal sets, set q
     // walking items [q items / kparts, (q+1) items / kparts) of its blocks
     // (dealt round-robin within the set) and writing its fp32 results to
@@ -341,7 +342,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
                         const float s_a0 = lds_read_f(lds_addr(&sab[m]));
                         const float S = s_a0 * 0.00390625f * swk[j];
                         v = S * (float)p;
-                        if (DEBUG_P && m < a.M && n < a.N) a.psum[(int64_t)m * a.N + n] = p >> 8;
+                        if (DEBUG_P && m < a.M && n < a.N)
+                            if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, 1, 0)) *d = p >> 8;
                     } else {
                         v = 0.0f;
 #pragma unroll
@@ -443,7 +445,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kouter_kernel(KouterArgs a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = 16 * mt + m_out + r;
-                        if (m < a.M && n < a.N) a.psum[((int64_t)m * a.N + n) * a.G + gj] = P[r] >> 8;
+                        if (m < a.M && n < a.N)
+                            if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, a.G, gj)) *d = P[r] >> 8;
                     }
                 }
             }
@@ -587,10 +590,12 @@ hipError_t launch_gemm_kouter(const GemmProblem& p, hipStream_t stream)
     s.y16 = static_cast<_Float16*>(p.y16);
     s.y32 = p.y32;
     s.psum = p.psum;
+    s.prows = p.prows;
     s.kparts = kouter_kparts(p);
     s.part = static_cast<float*>(p.ws);
-    // the split needs its workspace, and is not used for the debug sums
-    if (s.kparts > 1 && (p.psum || !p.ws || p.ws_bytes < kouter_workspace_bytes(p))) s.kparts = 1;
+    // the split needs its workspace (each half writes the debug sums of its
+    // own groups)
+    if (s.kparts > 1 && (!p.ws || p.ws_bytes < kouter_workspace_bytes(p))) s.kparts = 1;
     if (s.kparts == 1) s.part = nullptr;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     const bool dbg = p.psum != nullptr;

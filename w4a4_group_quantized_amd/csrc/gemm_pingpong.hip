@@ -93,6 +93,7 @@ struct PPArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
     // Tiles: BM x BN blocks of Y in row-major order over the tile grid;
     // workgroup b of a launch takes tile tile0 + b (full K, the epilogue
     // writes Y) or, in a K-split launch (part != null), tile tile0 + b % ntail
@@ -414,8 +415,10 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         if (ends) scale_products(buf);
     };
 
-    // Vector phase: acc += S (.) P for the finished group j.  The anchors
-    // keep the conversion and the updates between this phase's barriers.
+    // Vector phase: acc += S (.) P for the finished group j (counted from
+    // this workgroup's first stage s0; the debug sums take the index over all
+    // of K).  The anchors keep the conversion and the updates between this
+    // phase's barriers.
     auto rescale = [&](int j) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -439,11 +442,13 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                     acc[mt][nt][r] = fmaf(S[mt][nt][r], (float)P[mt][nt][r], acc[mt][nt][r]);
                 if (DEBUG_P) {
                     const int n = n0 + wn * 64 + nt * 32 + (lane & 31);
+                    const int jg = SPG == 0 ? j : s0 / SPG + j;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
                         if (m < a.M && n < a.N)
-                            a.psum[((int64_t)m * a.N + n) * a.G + j] = F8 ? (int)P[mt][nt][r] : (int)P[mt][nt][r] >> 8;
+                            if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, a.G, jg))
+                                *d = F8 ? (int)P[mt][nt][r] : (int)P[mt][nt][r] >> 8;
                     }
                 }
             }
@@ -564,7 +569,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         rescale(0);
     } else if (!EARLY && SPG == 1) {
         // the last stage ends the last group
-        rescale(a.G - 1);
+        rescale(stages - 1);
     }
 
     if (a.part) {
@@ -758,6 +763,7 @@ hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
     t.psum = p.psum;
+    t.prows = p.prows;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.nparts = 1;
     const int tiles = ((p.M + BM - 1) / BM) * t.tiles_n;
@@ -784,14 +790,16 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
     t.psum = p.psum;
+    t.prows = p.prows;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.tile0 = 0;
     t.ntail = 0;
     t.nparts = 1;
     t.part = nullptr;
     PingpongSplit sp = pingpong_split(p);
-    // the K split needs its workspace, and is not used for the debug sums
-    if (sp.tail && (p.psum || !p.ws || p.ws_bytes < sp.bytes)) sp.tail = 0;
+    // the K split needs its workspace (each part writes the debug sums of
+    // its own groups)
+    if (sp.tail && (!p.ws || p.ws_bytes < sp.bytes)) sp.tail = 0;
     sp.part = static_cast<float*>(p.ws);
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     // mixed mode here: ga = 128 or 256 (the activation groups are 1 or 2 stages)

@@ -46,6 +46,7 @@ struct SkinnyArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
 };
 
 __device__ inline v4i widen_lo(uint4 w)
@@ -268,7 +269,8 @@ __global__ __launch_bounds__(W * 64, MT <= 3 ? 4 : 2) void gemm_skinny_kernel(Sk
                             for (int r = 0; r < 4; ++r) {
                                 const int m = 16 * mt + 4 * kb + r;
                                 if (m < a.M && n < a.N)
-                                    a.psum[((int64_t)m * a.N + n) * a.G + j] = P[mt][nt][r] >> 8;
+                                    if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, a.G, j))
+                                        *d = P[mt][nt][r] >> 8;
                             }
                         }
                 }
@@ -300,7 +302,8 @@ __global__ __launch_bounds__(W * 64, MT <= 3 ? 4 : 2) void gemm_skinny_kernel(Sk
                 const int64_t off = (int64_t)m * a.N + n;
                 a.y16[off] = (_Float16)v;
                 if (a.y32) a.y32[off] = v;
-                if (DEBUG_P) a.psum[off] = p >> 8;
+                if (DEBUG_P)
+                    if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, 1, 0)) *d = p >> 8;
             }
         }
         return;
@@ -420,6 +423,7 @@ hipError_t launch_gemm_skinny(const GemmProblem& p, hipStream_t stream)
     s.y16 = static_cast<_Float16*>(p.y16);
     s.y32 = p.y32;
     s.psum = p.psum;
+    s.prows = p.prows;
     const bool mixed = (p.gw == p.K) && (p.ga != p.gw);
     const bool one = s.gs == p.K;
     const bool dbg = p.psum != nullptr;

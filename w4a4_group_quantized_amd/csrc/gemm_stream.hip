@@ -62,6 +62,7 @@ struct StreamArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
 };
 
 // One item in LDS: 16 weight-row pieces, ACT activation-row pieces (ACT = 4,
@@ -305,7 +306,8 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
                     for (int w = 0; w < WAVES; ++w) p += __builtin_bit_cast(int, v8[w]);
                     const float S = s_a0 * 0.00390625f * s_w0;
                     v = S * (float)p;
-                    if (DEBUG_P) a.psum[(int64_t)m * a.N + n] = p >> 8;
+                    if (DEBUG_P)
+                        if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, 1, 0)) *d = p >> 8;
                 } else {
                     v = 0.0f;
 #pragma unroll
@@ -401,7 +403,8 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(StreamArgs a)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (m_out + r < a.M && n < a.N)
-                                a.psum[((int64_t)(m_out + r) * a.N + n) * a.G + j] = P[q][r] >> 8;
+                                if (int32_t* d = psum_at(a.psum, a.prows, m_out + r, n, a.N, a.G, j))
+                                    *d = P[q][r] >> 8;
                     }
                 }
             }
@@ -491,6 +494,7 @@ hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream)
     s.y16 = static_cast<_Float16*>(p.y16);
     s.y32 = p.y32;
     s.psum = p.psum;
+    s.prows = p.prows;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
     const bool dbg = p.psum != nullptr;
     if (mixed) return launch_gm<1, true>(s, dbg, stream);

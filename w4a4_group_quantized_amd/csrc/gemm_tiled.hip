@@ -79,6 +79,7 @@ struct TileArgs {
     _Float16* y16;
     float* y32;
     int32_t* psum;
+    PsumRows prows;
 };
 
 __device__ inline uint4 widen_lo(uint4 w)
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_tiled_kernel(TileArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
-                if (m < a.M && n < a.N) a.psum[((int64_t)m * a.N + n) * a.G + j] = P[mt][nt][r] >> 8;
+                if (m < a.M && n < a.N)
+                    if (int32_t* d = psum_at(a.psum, a.prows, m, n, a.N, a.G, j)) *d = P[mt][nt][r] >> 8;
             }
         }
     };
@@ -566,6 +568,7 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream)
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
     t.psum = p.psum;
+    t.prows = p.prows;
     const bool mixed = (p.gw == p.K) && (p.ga != p.gw);
     if (t.gs == 32)
         launch_tiled_mode<1>(t, mixed, stream);

@@ -11,6 +11,26 @@ namespace apex4 {
 hipError_t launch_quantize(const void* x_f16, int64_t rows, int64_t K, int32_t g,
                            void* q_u8, float* s, hipStream_t stream);
 
+// Rows of the debug group sums: output row m goes to row (m - row0) / step of
+// psum when that is a whole number below count; row0 = 0, step = 1, count = M
+// keeps every row.  psum is then int32 [count, N, G].
+struct PsumRows {
+    int32_t row0 = 0;
+    int32_t step = 1;
+    int32_t count = 0;
+};
+
+// The address of the debug sum of (m, n, group j), or null for rows that are
+// not kept.
+__device__ inline int32_t* psum_at(int32_t* psum, const PsumRows& pr, int m, int n, int N, int G, int j)
+{
+    const int d = m - pr.row0;
+    if (d < 0) return nullptr;
+    const int q = d / pr.step;
+    if (q * pr.step != d || q >= pr.count) return nullptr;
+    return psum + ((int64_t)q * N + n) * G + j;
+}
+
 struct GemmProblem {
     const uint8_t* qa;
     const float* sa;
@@ -20,7 +40,8 @@ struct GemmProblem {
     int32_t ga, gw;       // group sizes along K of the two operands
     void* y16;            // fp16 [M, N]
     float* y32;           // fp32 [M, N] or null
-    int32_t* psum;        // int32 [M, N, K/min(ga,gw)] or null
+    int32_t* psum;        // int32 [prows.count, N, K/min(ga,gw)] or null
+    PsumRows prows;       // which output rows psum keeps
     void* ws;             // device workspace (gemm_workspace_bytes) or null
     size_t ws_bytes;
 };
@@ -53,6 +74,14 @@ size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
 hipError_t launch_gemm_tiled(const GemmProblem& p, hipStream_t stream);
+
+// apex4_gemm_w4a4 / apex4_gemm_w4a4_debug after their own checks: every
+// documented host-side check of the GEMM, then launch_gemm on `stream`.
+// Returns an apex4_status code.
+int32_t gemm_checked(const void* qa_u8, const float* s_a, int32_t group_a, const void* qw_u8, const float* s_w,
+                     int32_t group_w, int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32, int64_t p_row0,
+                     int64_t p_step, int64_t p_rows, int32_t* psum_dbg, void* workspace, size_t workspace_bytes,
+                     void* stream);
 bool pingpong_supports(const GemmProblem& p);
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
 // FP8-coded operands (apex4_gemm_w4a4_f8): qa, qw hold one E4M3 byte per code

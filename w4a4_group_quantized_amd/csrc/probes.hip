@@ -1,6 +1,7 @@
 // Measurement probes (include/apex4_probe.h): the int8 matrix-unit rate, the
-// HBM read rate and the fp32 vector-ALU rate of the GPU at hand, the ceilings
-// the GEMM kernels are quoted against besides the datasheet peaks.
+// HBM read rate, the fp32 vector-ALU rate and the LDS read rate of the GPU at
+// hand, the ceilings the GEMM kernels are quoted against besides the datasheet
+// peaks.
 #include "apex4_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -71,6 +72,47 @@ __global__ __launch_bounds__(PROBE_THREADS) void probe_valu_kernel(int64_t iters
     if (s == -12345.0f) sink[0] = s;
 }
 
+// 16-byte LDS reads: every wave reads 1 KB contiguous pieces (lane l at 16 l:
+// no bank conflicts) of a 16 KB buffer, 8 reads per iteration issued
+// together and waited for in the same asm statement (so none can be hoisted
+// out of the loop and no result is used before it has arrived); 16 waves per
+// compute unit keep many reads in flight.
+constexpr int LDS_PROBE_BYTES = 16384;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(PROBE_THREADS) void probe_lds_kernel(int64_t iters, int32_t* sink)
+{
+    __shared__ uint4 buf[LDS_PROBE_BYTES / 16];
+    const int t = threadIdx.x, lane = t & 63;
+    for (int i = t; i < LDS_PROBE_BYTES / 16; i += PROBE_THREADS)
+        buf[i] = make_uint4(i, 3 * i + 1, 5 * i + 2, 7 * i + 3);
+    __syncthreads();
+    // byte address of this lane's 16 bytes in piece 0; the 8 reads take
+    // pieces 0..7 (or 8..15 on odd iterations) at immediate offsets
+    const uint32_t base = (uint32_t)(uintptr_t)buf + 16u * lane;
+    u32x4 acc = {0, 0, 0, 0};
+    for (int64_t i = 0; i < iters; ++i) {
+        const uint32_t a = base + (((uint32_t)i & 1u) << 13);
+        u32x4 v0, v1, v2, v3, v4, v5, v6, v7;
+        asm volatile(
+            "ds_read_b128 %0, %8\n"
+            "ds_read_b128 %1, %8 offset:1024\n"
+            "ds_read_b128 %2, %8 offset:2048\n"
+            "ds_read_b128 %3, %8 offset:3072\n"
+            "ds_read_b128 %4, %8 offset:4096\n"
+            "ds_read_b128 %5, %8 offset:5120\n"
+            "ds_read_b128 %6, %8 offset:6144\n"
+            "ds_read_b128 %7, %8 offset:7168\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+            : "v"(a)
+            : "memory");
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+        acc += v4 ^ v5 ^ v6 ^ v7;
+    }
+    const uint32_t s = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (s == 0x7fffffffu) sink[0] = (int32_t)s;
+}
+
 apex4_status launched()
 {
     return hipGetLastError() == hipSuccess ? APEX4_OK : APEX4_ERR_HIP;
@@ -112,6 +154,17 @@ apex4_status apex4_probe_valu_f32(int64_t iters, float* sink, double* flops_out,
     if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
     *flops_out = (double)PROBE_BLOCKS * PROBE_THREADS * (double)iters * 8 * 2;
     probe_valu_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
+    return launched();
+}
+
+apex4_status apex4_probe_lds_read(int64_t iters, int32_t* sink, double* bytes_out, void* stream)
+{
+    using namespace apex4;
+    if (iters < 1 || iters > (int64_t(1) << 30) || sink == nullptr || bytes_out == nullptr)
+        return APEX4_ERR_INVALID_ARG;
+    if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
+    *bytes_out = (double)PROBE_BLOCKS * PROBE_THREADS * (double)iters * 8 * 16;
+    probe_lds_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
     return launched();
 }
 

@@ -70,8 +70,15 @@ class W4A4Linear(torch.nn.Module):
         if not x2.is_contiguous():
             x2 = x2.contiguous()
         M = x2.shape[0]
-        y = apex4.linear(x2, self.group_a, self.qw, self.sw, self.group_w,
-                         y16=None if out is None else out.reshape(M, self.out_features),
+        y16 = None
+        if out is not None:
+            # the library writes M x out_features contiguous values: `out` must be
+            # exactly that memory (a reshape that copies would leave it unwritten)
+            if tuple(out.shape) != (*lead, self.out_features) or not out.is_contiguous():
+                raise ValueError(f"out must be a contiguous {(*lead, self.out_features)} tensor, "
+                                 f"got {tuple(out.shape)} (contiguous: {out.is_contiguous()})")
+            y16 = out.view(M, self.out_features)
+        y = apex4.linear(x2, self.group_a, self.qw, self.sw, self.group_w, y16=y16,
                          workspace=self._workspace(M, x2.device))
         return y.reshape(*lead, self.out_features)
 
