@@ -152,6 +152,30 @@ apex4_status apex4_gemm_w4a4_debug(const void* qa_u8, const float* s_a, int32_t 
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * apex4_gemm_w4a4 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * There is no workspace argument: the only scratch memory of the GEMM (the
+ * fp32 partial results of its K splits, see apex4_gemm_workspace_size) goes to
+ * an array the library holds in the memory of every GPU it runs on, of
+ * APEX4_NOALLOC_MAX_WORKSPACE bytes, from module load until the process ends.
+ * Arguments, checks, status codes and results are those of apex4_gemm_w4a4
+ * without debug sums (the same kernels and the same K splits, so the same
+ * bits).  A shape whose apex4_gemm_workspace_size() exceeds the array returns
+ * APEX4_ERR_WORKSPACE before anything is launched (on MI355X none does: the
+ * largest split takes one 256 x 128 fp32 tile per compute unit, 32 MiB on 256
+ * compute units).  The call itself allocates nothing; its first call on a
+ * device looks up that device's array address (hipGetSymbolAddress; a
+ * failure returns APEX4_ERR_HIP).  The array keeps the last call's contents
+ * and is fully rewritten before it is read; calls that overlap on one GPU
+ * (concurrent streams or threads) share it and race.
+ */
+#define APEX4_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+apex4_status apex4_gemm_w4a4_noalloc(const void* qa_u8, const float* s_a, int32_t group_a,
+                                     const void* qw_u8, const float* s_w, int32_t group_w,
+                                     int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                     void* stream);
+
+/*
  * One W4A4 linear layer call: Y = X * W^T with X quantized on the fly, i.e.
  * apex4_quantize_act(X) followed by apex4_gemm_w4a4 (the APEX4 page,
  * Abstract: activations quantized online, weights offline), with the same

@@ -263,3 +263,19 @@ def test_binding_refuses_mismatched_tensors():
         apex4.quantize_act(x, 128, out=(T((M, K // 2), torch.uint8), T((M, 1), torch.float32)))
     with pytest.raises(ValueError):
         apex4.quantize_act(x, 128, out=(T((M, K), torch.uint8), T((M, K // 128), torch.float32)))
+
+
+def test_noalloc_host_checks(L):
+    """apex4_gemm_w4a4_noalloc: the checks of apex4_gemm_w4a4 on the host,
+    before anything is looked up or launched; the scratch size in the header
+    and in the binding agree."""
+    f = L.apex4_gemm_w4a4_noalloc
+    assert f(A16, A16b, 128, A16, A16b, 128, 16, 16, 1000, A16b, None, None) == INVALID     # K % 128
+    assert f(A16, A16b, 96, A16, A16b, 96, 16, 16, 1024, A16b, None, None) == INVALID       # group
+    assert f(A16, A16b, 512, A16, A16b, 512, 16, 16, 1024, A16b, None, None) == UNSUPPORTED
+    assert f(A16, A16b, 128, A16, A16b, 128, 16, 16, 1024, None, None, None) == INVALID     # NULL y16
+    assert f(MIS, A16b, 128, A16, A16b, 128, 16, 16, 1024, A16b, None, None) == ALIGN
+    assert f(None, None, 128, A16, A16b, 128, 0, 16, 1024, None, None, None) == OK          # empty
+    text = open(os.path.join(ROOT, "include", "apex4.h")).read()
+    m = re.search(r"#define APEX4_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == apex4.NOALLOC_MAX_WORKSPACE

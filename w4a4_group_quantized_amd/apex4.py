@@ -16,6 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("APEX4_LIB", os.path.join(PKG, "libapex4.so"))
 
 OK = 0
+# APEX4_NOALLOC_MAX_WORKSPACE: the per-GPU scratch array of apex4_gemm_w4a4_noalloc
+NOALLOC_MAX_WORKSPACE = 32 << 20
 STATUS_NAMES = {0: "APEX4_OK", 1: "APEX4_ERR_INVALID_ARG", 2: "APEX4_ERR_UNSUPPORTED",
                 3: "APEX4_ERR_ALIGNMENT", 4: "APEX4_ERR_WORKSPACE", 5: "APEX4_ERR_HIP"}
 
@@ -32,6 +34,7 @@ SIGNATURES = {
                                _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_gemm_w4a4_debug": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64,
                                      _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "apex4_gemm_w4a4_noalloc": (_I32, [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P]),
     "apex4_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_linear_w4a4": (_I32, [_P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
@@ -180,6 +183,25 @@ def gemm(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, want_y32: bo
             _ptr(ws), ws_bytes, _stream(torch, dev)))
     if want_y32 or want_psum:
         return y16, y32, psum
+    return y16
+
+
+def gemm_noalloc(qa, sa, ga: int, qw, sw, gw: int, K: int | None = None, *, y16, y32=None):
+    """apex4_gemm_w4a4_noalloc: the GEMM into caller-provided outputs with no
+    workspace and no allocation (y16, and y32 when given, are written)."""
+    import torch
+    M, N = qa.shape[0], qw.shape[0]
+    K = 2 * qa.shape[1] if K is None else K
+    dev = qa.device
+    _need_gpu(qa, "qa", torch.uint8, (M, K // 2), dev)
+    _need_gpu(qw, "qw", torch.uint8, (N, K // 2), dev)
+    _need_gpu(sa, "s_a", torch.float32, (M, _cols(K, ga)), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, _cols(K, gw)), dev)
+    _need_gpu(y16, "y16", torch.float16, (M, N), dev)
+    if y32 is not None:
+        _need_gpu(y32, "y32", torch.float32, (M, N), dev)
+    _check("apex4_gemm_w4a4_noalloc", lib().apex4_gemm_w4a4_noalloc(
+        _ptr(qa), _ptr(sa), ga, _ptr(qw), _ptr(sw), gw, M, N, K, _ptr(y16), _ptr(y32), _stream(torch, dev)))
     return y16
 
 
