@@ -65,6 +65,9 @@ WORKLOADS = {
 # The same layer sets on FP8-coded operands (apex4_quantize_f8, apex4_gemm_w4a4_f8):
 # name -> the INT4 workload it mirrors
 F8_WORKLOADS = {"llama2-7b-prefill-f8": "llama2-7b-prefill", "llama2-70b-prefill-f8": "llama2-70b-prefill"}
+# ... and on FP6-coded operands (apex4_quantize_f6, apex4_gemm_w4a4_f6: each code a 6-bit E2M3 field)
+F6_WORKLOADS = {"llama2-7b-prefill-f6": "llama2-7b-prefill", "llama2-70b-prefill-f6": "llama2-70b-prefill",
+                "sweep-g128-f6": "sweep-g128"}
 # Decode with the activation quantization inside the GEMM launch (apex4_linear_w4a4,
 # 1-2 rows): name -> the two-call workload it mirrors
 FUSED_WORKLOADS = {"llama2-70b-decode-m1-fused": "llama2-70b-decode-m1"}
@@ -93,7 +96,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2-70b-prefill",
                     choices=sorted(WORKLOADS) + sorted(LAYER_WORKLOADS) + sorted(F8_WORKLOADS)
-                    + sorted(FUSED_WORKLOADS))
+                    + sorted(F6_WORKLOADS) + sorted(FUSED_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probes of the GPU's measured ceilings")
@@ -109,6 +112,11 @@ def parse():
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="CPU only: write profiles/hbm_traffic.json from the rocprofv3 counter "
                          "runs under DIR (pmc_<FETCH_SIZE|WRITE_SIZE>_<copy|workload>/)")
+    ap.add_argument("--modes", metavar="SHAPES",
+                    help="time the GEMM alone in every group mode on the given shapes "
+                         "(M:K:N,M:K:N,...; back-to-back launches, weights cycled past the "
+                         "last-level cache) and print one JSON line of rates per shape: the "
+                         "measurements behind apex4_select_granularity")
     ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
@@ -293,9 +301,11 @@ def write_traffic(prof_dir, workloads):
                           "bench.py reports them only while the sources of the workload's kernels hash the same.",
            "calibration": cal, "workloads": {}}
     for wl in workloads:
-        # (FP8-coded operands: one byte per code, (M + N) K / 2 more bytes read)
+        # (FP8-coded operands: one byte per code, (M + N) K / 2 more bytes read;
+        # FP6: (M + N) K / 4 more)
         f8 = wl in F8_WORKLOADS
-        _, M, layers, ga, gw, _ = WORKLOADS[F8_WORKLOADS.get(wl, wl)]
+        f6 = wl in F6_WORKLOADS
+        _, M, layers, ga, gw, _ = WORKLOADS[{**F8_WORKLOADS, **F6_WORKLOADS}.get(wl, wl)]
         fc, wc = step_calls("FETCH_SIZE", wl), step_calls("WRITE_SIZE", wl)
         names = {k for ks, _ in fc for k in ks}
         files = kernel_source_files(names)
@@ -307,7 +317,8 @@ def write_traffic(prof_dir, workloads):
             per.append({"M": M, "K": K, "N": N, "dispatches": len(f),
                         "fetch_bytes": sum(f) / len(f) * 1024 * cal["fetch_factor"],
                         "write_bytes": sum(w) / len(w) * 1024 * cal["write_factor"],
-                        "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)})
+                        "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)
+                        + ((M + N) * K / 4 if f6 else 0)})
         out["workloads"][wl] = {
             "kernel_sources": files,
             "kernel_sources_sha256": kernel_sources_sha256(files),
@@ -319,6 +330,68 @@ def write_traffic(prof_dir, workloads):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({w: out["workloads"][w]["hbm_bytes_per_launch"] for w in workloads}))
+
+
+# the group modes of apex4_select_granularity: (group_a, group_w), 0 = K
+MODES = [(32, 32), (64, 64), (128, 128), (128, 0), (256, 256), (0, 0)]
+
+
+def mode_rates(shapes):
+    """GEMM time of every group mode on each shape M:K:N, back-to-back
+    launches; one JSON line per shape with TOPS and TB/s per mode.
+    Compute-bound shapes (M >= 256) run on quantized LLaMA-like inputs
+    (outlier activations, N(0, 0.02) weights: the codes set the matrix
+    unit's power draw, hence its clock); memory-bound ones on random codes,
+    cycling enough weight copies to stream them from HBM."""
+    import torch
+    from w4a4_group_quantized_amd import apex4
+    dev = torch.device("cuda:0")
+    apex4.lib()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    for spec in shapes.split(","):
+        M, K, N = (int(v) for v in spec.split(":"))
+        row = {"M": M, "K": K, "N": N, "modes": {}}
+        fp16 = None
+        if M >= 256:
+            x, w = inputs.problem(M, N, K, seed=0, act="outlier")
+            fp16 = (t(x), t(w))
+            del x, w
+        for (ga, gw) in MODES:
+            ga_, gw_ = ga or K, gw or K
+            if K % min(ga_, gw_) or (ga_ == K and gw_ == K and K >= 1 << 17):
+                continue
+            bytes_ = rl.gemm_bytes(M, N, K, ga_, gw_)
+            if fp16 is not None:
+                copies = 1
+                ws = [apex4.quantize_act(fp16[0], ga_) + apex4.pack_weight(fp16[1], gw_)]
+            else:
+                copies = max(1, int(np.ceil(2**30 / bytes_)))
+                ws = []
+                for c in range(copies):
+                    qa, sa = inputs.random_packed(M, K, K // ga_, seed=2 * c)
+                    qw, sw = inputs.random_packed(N, K, K // gw_, seed=2 * c + 1)
+                    ws.append((t(qa), t(sa), t(qw), t(sw)))
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            R = max(copies, 8)
+
+            def run():
+                for r in range(R):
+                    qa, sa, qw, sw = ws[r % copies]
+                    apex4.gemm(qa, sa, ga_, qw, sw, gw_, K, y16=y)
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) * 1e-3 / (3 * R)
+            row["modes"][f"{ga}/{gw}"] = {"us": round(sec * 1e6, 2),
+                                         "tops": round(rl.gemm_ops(M, N, K) / sec / 1e12, 1),
+                                         "tbps": round(bytes_ / sec / 1e12, 3)}
+            del ws
+        print(json.dumps(row), flush=True)
 
 
 def measure_ceilings(torch, apex4):
@@ -364,6 +437,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.modes:
+        mode_rates(args.modes)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -377,11 +453,14 @@ def main():
     from w4a4_group_quantized_amd import apex4
 
     f8 = args.workload in F8_WORKLOADS
+    f6 = args.workload in F6_WORKLOADS
     fused = args.workload in FUSED_WORKLOADS
-    base = F8_WORKLOADS.get(args.workload, FUSED_WORKLOADS.get(args.workload, args.workload))
+    base = {**F8_WORKLOADS, **F6_WORKLOADS, **FUSED_WORKLOADS}.get(args.workload, args.workload)
     desc, M, layers, ga, gw, act = WORKLOADS[base]
     if f8:
         desc += ", FP8-coded operands (one E4M3 byte per INT4 code)"
+    if f6:
+        desc += ", FP6-coded operands (one 6-bit E2M3 field per INT4 code)"
     if fused:
         desc += ", one apex4_linear_w4a4 call per layer (activation quantization in the GEMM launch where K <= 8192)"
     dev = torch.device("cuda:0")
@@ -393,6 +472,11 @@ def main():
         pack = lambda tw: apex4.quantize_f8(tw, gw)
         gemm = lambda qa, sa, qw, sw, K, y: apex4.gemm_f8(qa, sa, qw, sw, y16=y)
         code_cols = lambda K: K
+    elif f6:
+        quant = lambda tx, out: apex4.quantize_f6(tx, ga, out=out)
+        pack = lambda tw: apex4.quantize_f6(tw, gw)
+        gemm = lambda qa, sa, qw, sw, K, y: apex4.gemm_f6(qa, sa, qw, sw, y16=y)
+        code_cols = lambda K: K * 3 // 4
     else:
         quant = lambda tx, out: apex4.quantize_act(tx, ga, out=out)
         pack = lambda tw: apex4.pack_weight(tw, gw)
@@ -416,7 +500,7 @@ def main():
             x, w = inputs.problem(M, N, K, seed=c, act=act)
             tx = torch.from_numpy(x).to(dev)
             qw, sw = pack(torch.from_numpy(w).to(dev))
-            qa = torch.empty((M, code_cols(K)), dtype=torch.uint8, device=dev)
+            qa = torch.empty((apex4.f6_rows(M) if f6 else M, code_cols(K)), dtype=torch.uint8, device=dev)
             sa = torch.empty((M, K // ga), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             data.append((K, N, tx, qa, sa, qw, sw, y))
@@ -424,9 +508,9 @@ def main():
     torch.cuda.synchronize()
 
     ops_step = sum(rl.gemm_ops(M, N, K) for (K, N) in layers)
-    # (FP8-coded operands: one byte per code instead of half; fused: the fp16
-    # rows are read in place of their codes and scales)
-    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)
+    # (FP8-coded operands: one byte per code instead of half; FP6: 3/4 byte;
+    # fused: the fp16 rows are read in place of their codes and scales)
+    bytes_gemm = [rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0) + ((M + N) * K / 4 if f6 else 0)
                   + (2 * M * K - M * K / 2 - 4 * M * K / ga if fused else 0) for (K, N) in layers]
 
     launch = torch.cuda.current_stream()
@@ -564,6 +648,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("int4 codes as e4m3 bytes on the fp8 MFMA (exact f32 sums), f32 rescale" if f8 else
+                  "int4 codes as e2m3 fields on the fp6 MFMA (exact f32 sums), f32 rescale" if f6 else
                   "int4 codes on i8 MFMA (i32 sums), f32 rescale"),
         "data": "synthetic",
         "config": {"workload": desc, "M": M, "layers_KN": layers, "group_a": ga, "group_w": gw,
@@ -576,7 +661,7 @@ def main():
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": float(np.mean(bytes_gemm)),
-                     "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else
+                     "kernel": "gemm (apex4_gemm_w4a4_f8)" if f8 else "gemm (apex4_gemm_w4a4_f6)" if f6 else
                      "fused quantize + gemm (apex4_linear_w4a4)" if fused else "gemm (apex4_gemm_w4a4)",
                      "kernel_avg_us": float(gemm_ms_avg.mean() * 1e3),
                      "kernel_timing": "event pair around every GEMM launch in the timed steps" if in_step

@@ -241,17 +241,78 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
                                 int32_t* psum_dbg, void* stream);
 
 /*
+ * FP6-coded operands: the same GEMM with each INT4 code stored as a 6-bit
+ * FP6 E2M3 field, the operand format gfx950's micro-scaling matrix
+ * instruction (v_mfma_scale_f32_32x32x64_f8f6f4) reads at twice its int8
+ * rate (the OSC page, Abstract, looks to 4-bit micro-scaling matrix hardware;
+ * the method is that of the APEX4 page, Abstract).  A code c in [-8, 7] is
+ * the field (c < 0) << 5 | |c|: with exponent bias 1 and 3 mantissa bits,
+ * the magnitudes 0..15 are the values 0/8 .. 15/8, so the field is c / 8
+ * exactly; the instruction's E8M0 block scales (2^3 on both operands) undo
+ * the 1/8, and its fp32 sum of products of such integers is exact.  The
+ * group sums P_j, and hence Y, are those of apex4_gemm_w4a4 on the same codes;
+ * the codes need no unpacking and the rescale no int -> fp32 conversion.  The
+ * price is 6 bits per code instead of 4.
+ *
+ * apex4_quantize_f6: the quantization rule of apex4_quantize_act /
+ * apex4_pack_weight (groups of 128), codes written as E2M3 fields (-0 is
+ * written as +0).  The 128 fields of a (row, group) pack little-endian into
+ * 96 bytes (code k of the group at bits 6k .. 6k+5), i.e. six 16-byte
+ * chunks.  Tiled layout: rows in blocks of 64, the last block padded with
+ * zero rows; the tile of row block b and group j is 6 KB at byte
+ * (b * K/128 + j) * 6144, and chunk q of row i of the block sits at
+ * + q * 1024 + i * 16 (each chunk of 64 rows is one contiguous KB, the piece
+ * the GEMM moves from memory to LDS in one load).
+ *   x_f16 [rows, K] fp16, 16-byte aligned; rows >= 0 (0: no-op), K % 128 == 0.
+ *   q6: ceil(rows/64)*64 * 3K/4 bytes (padding rows written as zeros),
+ *       16-byte aligned;  s [rows, K/128] fp32, as apex4_quantize_act.
+ *   group: 128 only (other valid groups: APEX4_ERR_UNSUPPORTED).
+ */
+apex4_status apex4_quantize_f6(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q6,
+                               float* s, void* stream);
+
+/*
+ * apex4_gemm_w4a4_f6: Y of apex4_gemm_w4a4 with group_a = group_w = 128 from
+ * FP6-coded operands (apex4_quantize_f6 outputs, tiled layout).
+ *   qa6: ceil(M/64)*64 * 3K/4 bytes, qw6: ceil(N/64)*64 * 3K/4 bytes, both
+ *   16-byte aligned, padding rows zero; s_a [M, K/128], s_w [N, K/128] fp32.
+ *   y_f16 [M, N], y_f32 [M, N] or NULL, psum_dbg [M, N, K/128] int32 or NULL
+ *   (M*N*K/128 < 2^31), as in apex4_gemm_w4a4.
+ *   workspace: at least apex4_gemm_workspace_size(M, N, K, 128, 128) bytes
+ *   (the same K split of a partial last round of 256x128 tiles), 16-byte
+ *   aligned, caller-owned.
+ *   M, N >= 0 (0: no-op), K > 0, K % 128 == 0, 4 * 6144 * K/128 < 2^31
+ *   (APEX4_ERR_UNSUPPORTED otherwise).  The kernel is the compute-bound one
+ *   (256 x 128 output tiles), meant for prefill-sized M.  Asynchronous on
+ *   `stream`; every check runs on the host before anything is launched.
+ */
+apex4_status apex4_gemm_w4a4_f6(const void* qa6, const float* s_a, const void* qw6, const float* s_w,
+                                int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                int32_t* psum_dbg, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Granularity selection for a GEMM shape on this GPU (APEX4 page, Abstract:
  * granularity adaptation by the GPU's matrix-to-vector throughput balance).
  * The modes, finest first: g = 32, 64, 128; mixed (group_a = 128, group_w =
- * K); g = 256; per-channel (g = K).  Each mode's time is modelled as
- *     max(bytes / 5.0e12 B/s,  2*M*N*K / rate(mode)),
- * bytes = M*K/2 + N*K/2 + 4*(M*K/group_a + N*K/group_w) + 2*M*N, with
- * rate(mode) the GEMM rate measured on MI355X for that mode (g = 32: 581,
- * 64: 834, 128: 1565, mixed: 1672, 256: 1750, K: 2316 TOPS), and the finest
- * mode whose modelled speed is at least min_rel_speed times the fastest
- * mode's is returned.  Modes whose groups do not divide K are skipped.
- * Host function: touches no device memory.
+ * K); g = 256; per-channel (g = K).  Each mode's time on the shape is modelled
+ * from GEMM rates measured on MI355X for the kernel apex4_gemm_w4a4 runs on
+ * that shape and mode:
+ *   - up to 64 rows with groups of at least 128 (the weight-streaming
+ *     kernels): bytes / rate, with the algorithmic bytes
+ *     M*K/2 + N*K/2 + 4*(M*K/group_a + N*K/group_w) + 2*M*N and the rate
+ *     interpolated (in log2 M) from the measured TB/s at M = 1, 4, 16, 64
+ *     (about 5.2, 4.3, 4.3, 2.0 TB/s);
+ *   - otherwise the tiled kernels, which work in whole 256-row tiles:
+ *     max(bytes / 5.0e12 B/s, 2*M'*N*K / rate) with M' = M rounded up to a
+ *     multiple of 256 and the rate interpolated from the measured TOPS at
+ *     M' = 256, 2048, 4096, 8192 (g = 32: 432..580, 64: 660..843, 128:
+ *     1333..1452, mixed: 1292..1570, 256: 1412..1663, K: 1838..2212).
+ * Groups of 32 and 64 have no weight-streaming kernel: at decode sizes they
+ * run on mostly empty 256-row tiles and are modelled (and measured) ten or
+ * more times slower.  The finest mode whose modelled speed is at least
+ * min_rel_speed times the fastest mode's is returned.  Modes whose groups do
+ * not divide K are skipped, and so is one group over K for K >= 2^17 (see
+ * apex4_gemm_w4a4).  Host function: touches no device memory.
  *   M, N >= 1; K >= 128, K % 128 == 0; 0 < min_rel_speed <= 1.
  *   group_a, group_w: HOST int32 outputs (group_w == K for per-channel
  *   weights), valid arguments for apex4_quantize_act / apex4_pack_weight /

@@ -1,7 +1,8 @@
 """apex4_select_granularity (include/apex4.h), a host function: the finest group
 mode whose modelled speed is within the asked fraction of the fastest mode's.
-The expected choices below follow from the documented model and rates by
-hand (no GPU needed)."""
+The expected choices below follow from the documented model and measured
+rates by hand (no GPU needed); tests/test_gpu_granularity.py checks the
+choices against GEMM times measured on the GPU."""
 import pytest
 
 from w4a4_group_quantized_amd import apex4
@@ -15,24 +16,40 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound: 1565/2316 = 0.676 >= 0.65 > 834/2316 = 0.36
+    # compute-bound, M = 2048: 1342/1883 = 0.713 >= 0.65 > 759/1883 = 0.40 (g=64)
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # mixed 1672/2316 = 0.722 qualifies at 0.70 (g=128, 0.676, does not);
-    # at 0.75 only g=256 (1750/2316 = 0.756) and coarser do; at 0.8 only g=K
+    # M = 8192: mixed 1570/2212 = 0.710 qualifies at 0.70 (g=128, 0.656, does
+    # not); at 0.75 only g=256 (1663/2212 = 0.752) and coarser do; at 0.8 only g=K
     assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
     assert apex4.select_granularity(8192, 28672, 8192, 0.80) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 
 
-def test_decode_affords_fine_groups():
-    # memory-bound: g=32 costs only its scale bytes, 1/(1 + 8/32) = 0.8 of g=K
-    assert apex4.select_granularity(1, 28672, 8192, 0.75) == (32, 32)
-    # g=64: 1/(1 + 8/64) = 0.89; g=32 (0.8) fails at 0.85
-    assert apex4.select_granularity(1, 28672, 8192, 0.85) == (64, 64)
+def test_decode_picks_a_streaming_mode():
+    # M = 1, N = 28672, K = 8192: the streaming kernels read ~118-125 MB at
+    # ~5.2 TB/s (mixed mode fastest, 22.4 us; g=128 23.6 us, 0.95 of it); g=32
+    # and g=64 run on 256-row tiles (~180-280 us)
+    assert apex4.select_granularity(1, 28672, 8192, 0.75) == (128, 128)
+    assert apex4.select_granularity(1, 28672, 8192, 0.96) == (128, 8192)
+    for M in (1, 4, 16, 64):
+        for r in (0.5, 0.75, 0.9):
+            ga, gw = apex4.select_granularity(M, 28672, 8192, r)
+            assert min(ga, gw) >= 128, (M, r, ga, gw)
+
+
+def test_decode_fine_groups_only_on_a_tiny_budget():
+    # accepting 20x slower than the fastest mode admits the tiled g=32 (0.08)
+    assert apex4.select_granularity(1, 28672, 8192, 0.05) == (32, 32)
+
+
+def test_one_group_over_large_k_not_offered():
+    # per-channel scales keep one int32 sum over K: refused from K = 2^17
+    assert apex4.select_granularity(2048, 4096, 1 << 17, 1.0) != (1 << 17, 1 << 17)
+    assert apex4.select_granularity(2048, 4096, (1 << 17) - 128, 1.0) == ((1 << 17) - 128, (1 << 17) - 128)
 
 
 def test_modes_that_do_not_divide_k_are_skipped():

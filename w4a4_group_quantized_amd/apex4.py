@@ -39,6 +39,8 @@ SIGNATURES = {
     "apex4_linear_w4a4": (_I32, [_P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "apex4_gemm_w4a4_f8": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "apex4_quantize_f6": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "apex4_gemm_w4a4_f6": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
                                         ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
@@ -284,6 +286,59 @@ def gemm_f8(qa8, sa, qw8, sw, *, want_y32: bool = False, want_psum: bool = False
     _check("apex4_gemm_w4a4_f8", lib().apex4_gemm_w4a4_f8(
         _ptr(qa8), _ptr(sa), _ptr(qw8), _ptr(sw), M, N, K, _ptr(y16), _ptr(y32), _ptr(psum),
         _stream(torch, dev)))
+    if want_y32 or want_psum:
+        return y16, y32, psum
+    return y16
+
+
+def f6_rows(rows: int) -> int:
+    """Rows of an FP6-coded operand buffer: whole blocks of 64 (apex4_quantize_f6's tiled layout)."""
+    return (rows + 63) // 64 * 64
+
+
+def quantize_f6(x, group: int = 128, out=None):
+    """x: fp16 [rows, K] GPU tensor -> (q6 uint8 [f6_rows(rows), 3K/4] E2M3 codes in the tiled
+    layout of apex4_quantize_f6, s float32 [rows, K/group])."""
+    import torch
+    _need_gpu(x, "x", torch.float16)
+    rows, K = x.shape
+    if out is None:
+        q6 = torch.empty((f6_rows(rows), K * 3 // 4), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, _cols(K, group)), dtype=torch.float32, device=x.device)
+    else:
+        q6, s = out
+        _need_gpu(q6, "q6", torch.uint8, (f6_rows(rows), K * 3 // 4), x.device)
+        _need_gpu(s, "s", torch.float32, (rows, _cols(K, group)), x.device)
+    _check("apex4_quantize_f6", lib().apex4_quantize_f6(
+        _ptr(x), rows, K, group, _ptr(q6), _ptr(s), _stream(torch, x.device)))
+    return q6, s
+
+
+def gemm_f6(qa6, sa, qw6, sw, *, want_y32: bool = False, want_psum: bool = False, y16=None, y32=None):
+    """apex4_gemm_w4a4_f6: the W4A4 GEMM (groups of 128) on FP6-coded operands (tiled layout);
+    M, N and K come from the scales.  Returns y16, or (y16, y32, psum) when want_y32/want_psum is set."""
+    import torch
+    M, N = sa.shape[0], sw.shape[0]
+    K = sa.shape[1] * 128
+    dev = qa6.device
+    _need_gpu(qa6, "qa6", torch.uint8, (f6_rows(M), K * 3 // 4), dev)
+    _need_gpu(qw6, "qw6", torch.uint8, (f6_rows(N), K * 3 // 4), dev)
+    _need_gpu(sa, "s_a", torch.float32, (M, K // 128), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, K // 128), dev)
+    if y16 is not None:
+        _need_gpu(y16, "y16", torch.float16, (M, N), dev)
+    if y32 is not None:
+        _need_gpu(y32, "y32", torch.float32, (M, N), dev)
+    if y16 is None:
+        y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if want_y32 and y32 is None:
+        y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    psum = torch.empty((M, N, K // 128), dtype=torch.int32, device=dev) if want_psum else None
+    ws_bytes = workspace_size(M, N, K, 128, 128)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    _check("apex4_gemm_w4a4_f6", lib().apex4_gemm_w4a4_f6(
+        _ptr(qa6), _ptr(sa), _ptr(qw6), _ptr(sw), M, N, K, _ptr(y16), _ptr(y32), _ptr(psum),
+        _ptr(ws), ws_bytes, _stream(torch, dev)))
     if want_y32 or want_psum:
         return y16, y32, psum
     return y16

@@ -187,6 +187,52 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
     return to_status(apex4::launch_gemm_pingpong_f8(p, static_cast<hipStream_t>(stream)));
 }
 
+apex4_status apex4_quantize_f6(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q6, float* s,
+                               void* stream)
+{
+    if (group != 128) return group > 0 && K > 0 && K % group == 0 ? APEX4_ERR_UNSUPPORTED : APEX4_ERR_INVALID_ARG;
+    const apex4_status st = check_quantize(x_f16, rows, K, group, q6, s);
+    if (st != APEX4_OK || rows == 0) return st;
+    if (!aligned(q6, 16)) return APEX4_ERR_ALIGNMENT;
+    return to_status(apex4::launch_quantize_f6(x_f16, rows, K, q6, s, static_cast<hipStream_t>(stream)));
+}
+
+apex4_status apex4_gemm_w4a4_f6(const void* qa6, const float* s_a, const void* qw6, const float* s_w, int64_t M,
+                                int64_t N, int64_t K, void* y_f16, float* y_f32, int32_t* psum_dbg,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
+        return APEX4_ERR_INVALID_ARG;
+    if (psum_dbg && (unsigned __int128)M * (uint64_t)N * (uint64_t)(K / 128) > (uint64_t)kMaxDim)
+        return APEX4_ERR_INVALID_ARG;
+    apex4::GemmProblem p{};
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.ga = 128;
+    p.gw = 128;
+    // 32-bit offsets within a 256-row block of operand bytes
+    if (!apex4::f6_supports(p)) return APEX4_ERR_UNSUPPORTED;
+    const size_t need = apex4_gemm_workspace_size(M, N, K, 128, 128);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return APEX4_ERR_WORKSPACE;
+    if (M == 0 || N == 0) return APEX4_OK;
+    if (!qa6 || !s_a || !qw6 || !s_w || !y_f16) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(qa6, 16) || !aligned(qw6, 16) || !aligned(s_a, 4) || !aligned(s_w, 4) || !aligned(y_f16, 2) ||
+        !aligned(y_f32, 4) || !aligned(psum_dbg, 4) || !aligned(workspace, 16))
+        return APEX4_ERR_ALIGNMENT;
+    p.qa = static_cast<const uint8_t*>(qa6);
+    p.sa = s_a;
+    p.qw = static_cast<const uint8_t*>(qw6);
+    p.sw = s_w;
+    p.y16 = y_f16;
+    p.y32 = y_f32;
+    p.psum = psum_dbg;
+    p.prows.count = static_cast<int32_t>(M);
+    p.ws = workspace;
+    p.ws_bytes = workspace_bytes;
+    return to_status(apex4::launch_gemm_f6(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t apex4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w)
 {
     // shapes apex4_gemm_w4a4 rejects, or that launch nothing, need none

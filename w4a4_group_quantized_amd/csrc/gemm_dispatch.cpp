@@ -10,39 +10,43 @@
 
 namespace apex4 {
 
+GemmKernel gemm_kernel(const GemmProblem& p)
+{
+    if (p.M <= 2 && gemv_supports(p)) return GemmKernel::Gemv;
+#ifndef APEX4_NO_STREAM
+    if (stream_supports(p)) return GemmKernel::Stream;
+#endif
+    if (gemv_supports(p)) return GemmKernel::Gemv;
+#ifndef APEX4_NO_KOUTER
+    if (kouter_supports(p)) return GemmKernel::Kouter;
+#endif
+    if (skinny_supports(p)) return GemmKernel::Skinny;
+#ifndef APEX4_NO_PINGPONG
+    if (pingpong_supports(p)) return GemmKernel::Pingpong;
+#endif
+    return GemmKernel::Tiled;
+}
+
 size_t gemm_workspace_bytes(const GemmProblem& p)
 {
-    // mirrors the order of launch_gemm: the K-outer and ping-pong kernels' K splits
-    if (p.M <= 2 && gemv_supports(p)) return 0;
-#ifndef APEX4_NO_STREAM
-    if (stream_supports(p)) return 0;
-#endif
-    if (gemv_supports(p)) return 0;
-#ifndef APEX4_NO_KOUTER
-    if (kouter_supports(p)) return kouter_workspace_bytes(p);
-#endif
-    if (skinny_supports(p)) return 0;
-#ifndef APEX4_NO_PINGPONG
-    if (pingpong_supports(p)) return pingpong_split(p).bytes;
-#endif
-    return 0;
+    // the K-outer and ping-pong kernels' K splits
+    switch (gemm_kernel(p)) {
+    case GemmKernel::Kouter: return kouter_workspace_bytes(p);
+    case GemmKernel::Pingpong: return pingpong_split(p).bytes;
+    default: return 0;
+    }
 }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream)
 {
-    if (p.M <= 2 && gemv_supports(p)) return launch_gemm_gemv(p, stream);
-#ifndef APEX4_NO_STREAM
-    if (stream_supports(p)) return launch_gemm_stream(p, stream);
-#endif
-    if (gemv_supports(p)) return launch_gemm_gemv(p, stream);
-#ifndef APEX4_NO_KOUTER
-    if (kouter_supports(p)) return launch_gemm_kouter(p, stream);
-#endif
-    if (skinny_supports(p)) return launch_gemm_skinny(p, stream);
-#ifndef APEX4_NO_PINGPONG
-    if (pingpong_supports(p)) return launch_gemm_pingpong(p, stream);
-#endif
-    return launch_gemm_tiled(p, stream);
+    switch (gemm_kernel(p)) {
+    case GemmKernel::Gemv: return launch_gemm_gemv(p, stream);
+    case GemmKernel::Stream: return launch_gemm_stream(p, stream);
+    case GemmKernel::Kouter: return launch_gemm_kouter(p, stream);
+    case GemmKernel::Skinny: return launch_gemm_skinny(p, stream);
+    case GemmKernel::Pingpong: return launch_gemm_pingpong(p, stream);
+    default: return launch_gemm_tiled(p, stream);
+    }
 }
 
 }  // namespace apex4

@@ -62,6 +62,12 @@ PingpongSplit pingpong_split(const GemmProblem& p);
 int kouter_kparts(const GemmProblem& p);
 size_t kouter_workspace_bytes(const GemmProblem& p);
 
+// The kernel launch_gemm runs for a shape (shapes and groups only): the
+// weight-streaming kernels for few rows (row-streaming dot8, LDS-streaming
+// MFMA, its K-outer variant, skinny MFMA), the tiled ones otherwise.
+enum class GemmKernel { Gemv, Stream, Kouter, Skinny, Pingpong, Tiled };
+GemmKernel gemm_kernel(const GemmProblem& p);
+
 // Device workspace the call needs (0 for most shapes): the kernel choice of
 // launch_gemm, shapes only.
 size_t gemm_workspace_bytes(const GemmProblem& p);
@@ -86,6 +92,11 @@ bool pingpong_supports(const GemmProblem& p);
 hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream);
 // FP8-coded operands (apex4_gemm_w4a4_f8): qa, qw hold one E4M3 byte per code
 hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream);
+// FP6-coded operands (apex4_gemm_w4a4_f6): qa, qw hold one 6-bit E2M3 field
+// per code, packed in K order ([rows, 3K/4] bytes); groups of 128
+bool f6_supports(const GemmProblem& p);
+hipError_t launch_gemm_f6(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_quantize_f6(const void* x_f16, int64_t rows, int64_t K, void* q6, float* s, hipStream_t stream);
 hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* q8, float* s,
                               hipStream_t stream);
 bool gemv_supports(const GemmProblem& p);

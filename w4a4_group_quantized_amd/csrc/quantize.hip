@@ -56,6 +56,73 @@ __global__ __launch_bounds__(256) void quantize_groups_kernel(const half8* __res
     }
 }
 
+// FP6-coded operands.  A code c is the 6-bit E2M3 field (c < 0) << 5 | |c|:
+// with a 3-bit mantissa and exponent bias 1, the magnitudes 0..15 of that
+// field are the subnormal and first-binade values 0/8 .. 15/8, so the field
+// holds c / 8 exactly (-8 included; -0 is stored as +0).  The 128 fields of a
+// (row, group) pack little-endian into 96 bytes, code k of the group at bits
+// 6k .. 6k+5; those 96 bytes are six 16-byte chunks.  Tiled layout: rows in
+// blocks of 64 (the last block padded with zero rows); tile (row block b,
+// group j) is 6 KB at byte ((b * G + j) * 6) * 1024, chunk q of row i of the
+// block at + q * 1024 + i * 16.  A tile's chunk q of 64 rows is then one
+// contiguous KB: one direct-to-LDS load of the GEMM.
+//
+// One thread per (row, half group): 64 codes (eight 16-byte loads), the two
+// halves of a group in neighbouring lanes, 48 bytes out (chunks 3h .. 3h+2).
+__device__ inline uint32_t f6_field(uint32_t word, int i)
+{
+    const int c = (int)(word << (28 - 4 * i)) >> 28;
+    return (c < 0 ? 32u : 0u) | (uint32_t)(c < 0 ? -c : c);
+}
+
+__global__ __launch_bounds__(256) void quantize_f6_kernel(const half8* __restrict__ x, int64_t rows, int64_t K,
+                                                          int64_t n_threads, uint4* __restrict__ q,
+                                                          float* __restrict__ s)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t hpr = K / 64;                    // half groups per row
+    const int64_t r = t / hpr, hg = t - r * hpr;
+    const bool in = t < n_threads;
+    const bool live = in && r < rows;              // padding rows of the last block: zeros
+    half8 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = half8{};
+    if (live) {
+        const half8* xr = x + r * (K / 8) + 8 * hg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = xr[i];
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, absmax8(h[i]));
+    // the other half of the group: the neighbouring lane (K / 64 is even)
+    m = fmaxf(m, dpp_move<0xB1>(m));
+    const float scale = m / 7.0f;
+    const bool nz = m != 0.0f;
+    if (in) {
+        uint32_t o[12];
+#pragma unroll
+        for (int i = 0; i < 12; ++i) o[i] = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = quantize8(h[i], scale, nz && live);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t f = f6_field(w, k);
+                const int b = 6 * (8 * i + k);     // bit position in the 48 bytes
+                o[b / 32] |= f << (b % 32);
+                if (b % 32 > 26) o[b / 32 + 1] |= f >> (32 - b % 32);
+            }
+        }
+        const int64_t G = K / 128, j = hg >> 1, half = hg & 1;
+        uint4* tile = q + ((r >> 6) * G + j) * 6 * 64 + (r & 63);
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            tile[(3 * half + c) * 64] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+        if (live && half == 0) s[r * G + j] = nz ? scale : 0.0f;
+    }
+}
+
 // One group per row (per-channel scales, any K % 8 == 0): one block per row.
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const half8* __restrict__ x,
                                                             int64_t k8,
@@ -106,6 +173,20 @@ hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* 
     const int64_t n8 = rows * (K / 8);
     const unsigned blocks = (unsigned)((n8 + 255) / 256);
     quantize_groups_kernel<128, true><<<blocks, 256, 0, stream>>>(static_cast<const half8*>(x_f16), n8, q8, s);
+    return hipGetLastError();
+}
+
+}  // namespace apex4
+
+namespace apex4 {
+
+hipError_t launch_quantize_f6(const void* x_f16, int64_t rows, int64_t K, void* q6, float* s, hipStream_t stream)
+{
+    // rows padded to whole blocks of 64
+    const int64_t n_threads = (rows + 63) / 64 * 64 * (K / 64);
+    const unsigned blocks = (unsigned)((n_threads + 255) / 256);
+    quantize_f6_kernel<<<blocks, 256, 0, stream>>>(static_cast<const half8*>(x_f16), rows, K, n_threads,
+                                                   static_cast<uint4*>(q6), s);
     return hipGetLastError();
 }
 
