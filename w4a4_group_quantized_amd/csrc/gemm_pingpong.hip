@@ -94,13 +94,18 @@ struct PPArgs {
     float* y32;
     int32_t* psum;
     PsumRows prows;
-    // Tiles: BM x BN blocks of Y in row-major order over the tile grid;
-    // workgroup b of a launch takes tile tile0 + b (full K, the epilogue
+    // Tiles: BM x BN blocks of Y, numbered in bands of group_m row blocks:
+    // down a column of the band, then the next column (so that the
+    // workgroups in flight share few A and B blocks: fewer re-reads of B
+    // from HBM than in row-major order); workgroup b of a launch takes tile
+    // tile0 + b (full K, the epilogue
     // writes Y) or, in a K-split launch (part != null), tile tile0 + b % ntail
     // over K part q = b / ntail of nparts (stages [q S / nparts, (q+1) S /
     // nparts) of the S = K/128), writing its fp32 sums to part[q][b % ntail]
     // ([BM][BN], before s_w in mixed mode) for the reduction kernel.
     int tiles_n;       // tiles along N: ceil(N / BN)
+    int tiles_m;       // tiles along M: ceil(M / BM)
+    int group_m;       // row blocks per band of the tile order
     int tile0;
     int ntail;
     int nparts;
@@ -135,6 +140,19 @@ __device__ inline void split3(float s, uint32_t& x0, uint32_t& x1, uint32_t& x2)
     x1 = bf16_trunc_bits(r1);
     const float r2 = r1 - __builtin_bit_cast(float, x1 << 16);
     x2 = bf16_trunc_bits(r2);
+}
+
+// (row block, column block) of a tile id: bands of group_m row blocks, each
+// walked column by column
+__device__ inline void tile_coords(const PPArgs& a, int tile, int& by, int& bx)
+{
+    const int band = a.group_m * a.tiles_n;
+    const int g = tile / band;
+    const int first = g * a.group_m;
+    const int rows = min(a.group_m, a.tiles_m - first);
+    const int local = tile - g * band;
+    by = first + local % rows;
+    bx = local / rows;
 }
 
 // Register anchors.  An empty volatile asm that takes a value in and out keeps
@@ -204,7 +222,8 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         lin -= kpart * a.ntail;
     }
     const int tile = a.tile0 + lin;
-    const int by = tile / a.tiles_n, bx = tile - by * a.tiles_n;
+    int by, bx;
+    tile_coords(a, tile, by, bx);
     const int m0 = by * BM, n0 = bx * BN;
     const uint32_t rowbytes = F8 ? (uint32_t)a.K : (uint32_t)a.K / 2;
     // this workgroup's stages: s0 .. s0 + stages - 1
@@ -633,7 +652,8 @@ __global__ __launch_bounds__(256) void pp_split_reduce_kernel(PPArgs a)
     const int lin = idx / PER_TILE, rem = idx - lin * PER_TILE;
     const int row = rem / (BN / 4), col = (rem - row * (BN / 4)) * 4;
     const int tile = a.tile0 + lin;
-    const int by = tile / a.tiles_n, bx = tile - by * a.tiles_n;
+    int by, bx;
+    tile_coords(a, tile, by, bx);
     const int m = by * BM + row;
     if (m >= a.M) return;
     const size_t o0 = (size_t)lin * (BM * BN) + row * BN + col;
@@ -685,6 +705,11 @@ void launch_pp_all(const PPArgs& t, const PingpongSplit& sp, hipStream_t stream)
     launch_pp<MIXED, SPG>(k, sp.nparts * sp.tail, stream);
     pp_split_reduce_kernel<MIXED><<<(sp.tail * (BM * BN / 4) + 255) / 256, 256, 0, stream>>>(k);
 }
+
+// Row blocks per band of the tile order: 16 (a round of 256 workgroups then
+// covers 16 x 16 tiles: at K = 8192 their A and B blocks are 24 MB, against
+// 129 MB for one row block and 256 column blocks in row-major order).
+int tile_band_rows(int tiles_m) { return tiles_m < 16 ? tiles_m : 16; }
 
 int cu_count()
 {
@@ -765,6 +790,8 @@ hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
     t.psum = p.psum;
     t.prows = p.prows;
     t.tiles_n = (p.N + BN - 1) / BN;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.group_m = tile_band_rows(t.tiles_m);
     t.nparts = 1;
     const int tiles = ((p.M + BM - 1) / BM) * t.tiles_n;
     if (t.psum) gemm_pp_kernel<false, true, 1, true><<<tiles, THREADS, 0, stream>>>(t);
@@ -792,6 +819,8 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.psum = p.psum;
     t.prows = p.prows;
     t.tiles_n = (p.N + BN - 1) / BN;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.group_m = tile_band_rows(t.tiles_m);
     t.tile0 = 0;
     t.ntail = 0;
     t.nparts = 1;
