@@ -419,10 +419,12 @@ def measure_ceilings(torch, apex4):
         return max(rates)
 
     out = {"mfma_i8_TOPS": best(lambda: apex4.probe_mfma_i8(2000, isink)) / 1e12,
+           "mfma_f6_TFLOPs": best(lambda: apex4.probe_mfma_f6(2000, isink)) / 1e12,
            "hbm_read_GBps": best(lambda: apex4.probe_hbm_read(buf, isink)) / 1e9,
            "valu_f32_TFLOPs": best(lambda: apex4.probe_valu_f32(4000, fsink)) / 1e12,
            "lds_read_TBps": best(lambda: apex4.probe_lds_read(4000, isink)) / 1e12,
-           "method": "apex4_probe_* kernels: 4096 waves of independent v_mfma_i32_32x32x32_i8; "
+           "method": "apex4_probe_* kernels: 4096 waves of independent v_mfma_i32_32x32x32_i8 "
+                     "(and of FP6 v_mfma_scale_f32_32x32x64_f8f6f4); "
                      "whole-4KB-row reads of 2 GiB; 8 fp32 FMA chains per thread (no packed fp32); "
                      "conflict-free 16-byte LDS reads, 16 waves per CU"}
     del buf
@@ -613,7 +615,9 @@ def main():
     layer_ops = np.array([rl.gemm_ops(M, N, K) for (K, N) in layers])
     if bound == "mfma":
         achieved = float(layer_ops.sum() / (gemm_ms_avg.sum() * 1e-3)) / 1e12
-        peak = rl.PEAK_INT8_OPS / 1e12
+        # the contraction's own dtype: int8 MFMA (INT4 codes), fp8 (E4M3 bytes:
+        # the same 5.0 peak) or fp6 (E2M3 fields)
+        peak = (rl.PEAK_FP6_FLOPS if f6 else rl.PEAK_INT8_OPS) / 1e12
         unit = "TFLOP/s"
     else:
         achieved = float(np.sum(bytes_gemm) / (gemm_ms_avg.sum() * 1e-3)) / 1e9
@@ -630,7 +634,8 @@ def main():
     ceilings = None if args.no_ceilings else measure_ceilings(torch, apex4)
     measured = None
     if ceilings is not None:
-        measured = ceilings["mfma_i8_TOPS"] if bound == "mfma" else ceilings["hbm_read_GBps"]
+        measured = (ceilings["hbm_read_GBps"] if bound != "mfma" else
+                    ceilings["mfma_f6_TFLOPs"] if f6 else ceilings["mfma_i8_TOPS"])
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,9 +1,9 @@
 /*
- * apex4_probe.h -- measurement probes of libapex4.so: four kernels that
+ * apex4_probe.h -- measurement probes of libapex4.so: five kernels that
  * measure, on the GPU at hand, the ceilings the W4A4 GEMM kernels are held
- * against (the int8 matrix-unit rate, the HBM read rate, the fp32 vector-ALU
- * rate, the LDS read rate), so that a result can be quoted against the chip's measured ceiling
- * as well as its datasheet peak.  The APEX4 page (aiqbench news page,
+ * against (the int8 and FP6 matrix-unit rates, the HBM read rate, the fp32
+ * vector-ALU rate, the LDS read rate), so that a result can be quoted against
+ * the chip's measured ceiling as well as its datasheet peak.  The APEX4 page (aiqbench news page,
  * Abstract) frames the method by the balance of the matrix (Tensor Core) and
  * vector (CUDA Core) throughputs of a GPU; these probes measure that balance
  * here.
@@ -36,6 +36,16 @@ extern "C" {
  *            (1024 * 4 * iters * 4 * 2 * 32*32*32).
  */
 apex4_status apex4_probe_mfma_i8(int64_t iters, int32_t* sink, double* ops_out, void* stream);
+
+/*
+ * Independent v_mfma_scale_f32_32x32x64_f8f6f4 instructions on FP6 E2M3
+ * operands with unit block scales (the instruction apex4_gemm_w4a4_f6 runs):
+ * the same grid and rounds as apex4_probe_mfma_i8.
+ *   iters: >= 1.   sink: device int32[1], 4-byte aligned.
+ *   ops_out: HOST double, set to the floating-point operations issued
+ *            (1024 * 4 * iters * 4 * 2 * 32*32*64).
+ */
+apex4_status apex4_probe_mfma_f6(int64_t iters, int32_t* sink, double* ops_out, void* stream);
 
 /*
  * Streaming read of `bytes` bytes: every wave reads whole 4 KB rows (16 bytes

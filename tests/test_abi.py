@@ -159,6 +159,9 @@ def test_probe_validation(L):
     assert L.apex4_probe_mfma_i8(0, A16, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_mfma_i8(10, None, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_mfma_i8(10, MIS, ctypes.byref(d), None) == ALIGN
+    assert L.apex4_probe_mfma_f6(0, A16, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_mfma_f6(10, None, ctypes.byref(d), None) == INVALID
+    assert L.apex4_probe_mfma_f6(10, MIS, ctypes.byref(d), None) == ALIGN
     assert L.apex4_probe_valu_f32(0, A16, ctypes.byref(d), None) == INVALID
     assert L.apex4_probe_valu_f32(10, A16, None, None) == INVALID
     assert L.apex4_probe_lds_read(0, A16, ctypes.byref(d), None) == INVALID

@@ -37,6 +37,14 @@ def test_probe_mfma(dev):
     assert 100e12 < ops / t < 5.5e15
 
 
+def test_probe_mfma_f6(dev):
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ops, t = timed(lambda: apex4.probe_mfma_f6(500, sink))
+    assert ops == 1024 * 4 * 500 * 4 * 2 * 32 * 32 * 64
+    assert 100e12 < ops / t < 11e15
+    assert int(sink.item()) == 0
+
+
 def test_probe_hbm_read(dev):
     buf = torch.zeros(1 << 28, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)

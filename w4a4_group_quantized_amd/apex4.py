@@ -44,6 +44,7 @@ SIGNATURES = {
     "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
                                         ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "apex4_probe_mfma_i8": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "apex4_probe_mfma_f6": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_hbm_read": (_I32, [_P, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_valu_f32": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "apex4_probe_lds_read": (_I32, [_I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
@@ -367,6 +368,12 @@ def probe_mfma_i8(iters: int, sink) -> float:
     """Independent int8 MFMAs; returns the integer operations issued."""
     _need_gpu(sink, "sink")
     return _probe("apex4_probe_mfma_i8", iters, _ptr(sink))
+
+
+def probe_mfma_f6(iters: int, sink) -> float:
+    """Independent FP6 (E2M3) micro-scaling MFMAs; returns the floating-point operations issued."""
+    _need_gpu(sink, "sink")
+    return _probe("apex4_probe_mfma_f6", iters, _ptr(sink))
 
 
 def probe_hbm_read(buf, sink) -> float:

@@ -32,11 +32,13 @@
 // same permutation on both operands, so the group sum is unchanged, and each
 // lane's 48 bytes are three whole chunks.
 //
-// In window i of a stage a wave issues the two FP6 MFMAs of tile T_i, the
-// bf16 MFMA of its scale product S_i (exact three-piece bf16 splits of
-// 2^0 s_a and s_w, six of the nine cross products, as in the nibble
-// kernels), and between them the 16 fmas that fold the previous tile's group
-// sum into its accumulators.
+// In window i of a stage a wave issues the two FP6 MFMAs of tile T_i with
+// the bf16 MFMA of its scale product S_i between them (exact three-piece
+// bf16 splits of s_a and s_w, six of the nine cross products, as in the
+// nibble kernels), then the 16 fmas that fold the previous tile's group sum
+// into its accumulators: that sum was finished three matrix instructions
+// earlier, so the fold does not wait on it (folding it between this tile's
+// MFMAs, right after its last K-step was issued, stalled there).
 #include "internal.h"
 
 namespace apex4 {
@@ -87,8 +89,8 @@ struct F6Args {
 struct StageBuf {
     uint4 a[PLANES][BM];
     uint4 b[PLANES][BN];
-    uint4 ta[BM];
-    uint4 tb[BN];
+    uint2 ta[2][BM];
+    uint2 tb[2][BN];
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* p, uint32_t bytes)
@@ -208,11 +210,13 @@ __device__ __forceinline__ void f6_body(const F6Args& a, StageBuf& b0, StageBuf&
             uint32_t x0, x1, x2;
             split3(sc, x0, x1, x2);
             // slots 0..7: x0 x0 x0 x1 | x1 x2 0 0 (paired with y0 y1 y2 y0 | y1 y0 0 0)
-            d.ta[ht] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
+            d.ta[0][ht] = make_uint2(x0 | (x0 << 16), x0 | (x1 << 16));
+            d.ta[1][ht] = make_uint2(x1 | (x2 << 16), 0);
         } else if (has_scale) {
             uint32_t y0, y1, y2;
             split3(sc, y0, y1, y2);
-            d.tb[ht] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+            d.tb[0][ht] = make_uint2(y0 | (y1 << 16), y2 | (y0 << 16));
+            d.tb[1][ht] = make_uint2(y1 | (y0 << 16), 0);
         }
     };
 
@@ -274,10 +278,8 @@ __device__ __forceinline__ void f6_body(const F6Args& a, StageBuf& b0, StageBuf&
         v4s opa[2], opb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            opa[i] = *reinterpret_cast<const v4s*>(reinterpret_cast<const uint8_t*>(&d.ta[wm * 64 + 32 * i + trow]) +
-                                                   8 * thalf);
-            opb[i] = *reinterpret_cast<const v4s*>(reinterpret_cast<const uint8_t*>(&d.tb[wn * 64 + 32 * i + trow]) +
-                                                   8 * thalf);
+            opa[i] = __builtin_bit_cast(v4s, d.ta[thalf][wm * 64 + 32 * i + trow]);
+            opb[i] = __builtin_bit_cast(v4s, d.tb[thalf][wn * 64 + 32 * i + trow]);
         }
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
@@ -300,8 +302,8 @@ __device__ __forceinline__ void f6_body(const F6Args& a, StageBuf& b0, StageBuf&
             anchor16(Sp);
             // This tile's first K-step, its scale product (folded in the next
             // window), its second K-step: the second depends on the first,
-            // so the scale product goes between them.  The previous tile's
-            // fold is spread over the window.
+            // so the scale product goes between them.  Then the previous
+            // tile's fold.
             Pc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(step_operand(fa[mt], 0), step_operand(fb[nt], 0),
                                                                  v16f{}, FMT_FP6, FMT_FP6, 0, SCALE_E8M0, 0,
                                                                  SCALE_E8M0);
@@ -311,16 +313,17 @@ __device__ __forceinline__ void f6_body(const F6Args& a, StageBuf& b0, StageBuf&
             if (i == 1)
 #pragma unroll
                 for (int c = 0; c < 3; ++c) fa[1][c] = d.a[3 * thalf + c][wm * 64 + 32 + trow];
-            fold_quarter(Pp, Sp, pmt, pnt, 0);
-            fold_quarter(Pp, Sp, pmt, pnt, 1);
             fence_sched();
             S[i & 1] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(opa[mt], opb[nt], v16f{}, 0, 0, 0);
-            fold_quarter(Pp, Sp, pmt, pnt, 2);
-            fold_quarter(Pp, Sp, pmt, pnt, 3);
             fence_sched();
             Pc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(step_operand(fa[mt], 1), step_operand(fb[nt], 1),
                                                                  Pc, FMT_FP6, FMT_FP6, 0, SCALE_E8M0, 0, SCALE_E8M0);
             anchor16(Pc);
+            fence_sched();
+            fold_quarter(Pp, Sp, pmt, pnt, 0);
+            fold_quarter(Pp, Sp, pmt, pnt, 1);
+            fold_quarter(Pp, Sp, pmt, pnt, 2);
+            fold_quarter(Pp, Sp, pmt, pnt, 3);
             if (DEBUG_P && (i > 0 || t > 0)) debug_tile(Pp, pmt, pnt, i == 0 ? s0 + t - 1 : s0 + t);
             if (i == 3) store_scale(dn, s_next);
             fence_sched();

@@ -1,5 +1,5 @@
-// Measurement probes (include/apex4_probe.h): the int8 matrix-unit rate, the
-// HBM read rate, the fp32 vector-ALU rate and the LDS read rate of the GPU at
+// Measurement probes (include/apex4_probe.h): the int8 and FP6 matrix-unit
+// rates, the HBM read rate, the fp32 vector-ALU rate and the LDS read rate of the GPU at
 // hand, the ceilings the GEMM kernels are quoted against besides the datasheet
 // peaks.
 #include "apex4_probe.h"
@@ -11,6 +11,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int PROBE_BLOCKS = 1024;
 constexpr int PROBE_THREADS = 256;
@@ -34,6 +36,28 @@ __global__ __launch_bounds__(PROBE_THREADS) void probe_mfma_kernel(int64_t iters
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += c0[r] ^ c1[r] ^ c2[r] ^ c3[r];
     if (s == 0x7fffffff) sink[0] = s;
+}
+
+// The same with v_mfma_scale_f32_32x32x64_f8f6f4 on FP6 E2M3 operands
+// (format code 2 for both) and unit block scales (E8M0 127): the instruction
+// of the FP6-coded GEMM.  The operand registers hold lane-dependent bits; six
+// of the eight registers carry the 64 six-bit fields of a lane's row slice.
+__global__ __launch_bounds__(PROBE_THREADS) void probe_mfma_f6_kernel(int64_t iters, int32_t* sink)
+{
+    const int l = threadIdx.x;
+    const v8i a = v8i{l, 3 * l + 1, 5 * l + 2, 7 * l + 3, 9 * l + 4, 11 * l + 5, 0, 0};
+    const v8i b = v8i{13 * l + 7, 17 * l + 9, 19 * l + 11, 23 * l + 13, 29 * l + 15, 31 * l + 17, 0, 0};
+    v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int64_t i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 2, 2, 0, 127, 0, 127);
+        c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, 2, 2, 0, 127, 0, 127);
+        c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, 2, 2, 0, 127, 0, 127);
+        c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, 2, 2, 0, 127, 0, 127);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    if (s == 1234.5f) sink[0] = 1;
 }
 
 // Every wave reads whole 4 KB rows: lane l takes bytes [64 l, 64 l + 64) of a
@@ -132,6 +156,16 @@ apex4_status apex4_probe_mfma_i8(int64_t iters, int32_t* sink, double* ops_out, 
     if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
     *ops_out = (double)PROBE_BLOCKS * (PROBE_THREADS / 64) * (double)iters * 4 * 2 * 32.0 * 32 * 32;
     probe_mfma_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
+    return launched();
+}
+
+apex4_status apex4_probe_mfma_f6(int64_t iters, int32_t* sink, double* ops_out, void* stream)
+{
+    using namespace apex4;
+    if (iters < 1 || sink == nullptr || ops_out == nullptr) return APEX4_ERR_INVALID_ARG;
+    if (!aligned(sink, 4)) return APEX4_ERR_ALIGNMENT;
+    *ops_out = (double)PROBE_BLOCKS * (PROBE_THREADS / 64) * (double)iters * 4 * 2 * 32.0 * 32 * 64;
+    probe_mfma_f6_kernel<<<PROBE_BLOCKS, PROBE_THREADS, 0, (hipStream_t)stream>>>(iters, sink);
     return launched();
 }
 

@@ -17,6 +17,7 @@ from __future__ import annotations
 # MI355X published peaks (dense, no sparsity)
 PEAK_INT8_OPS = 5.0e15        # int8 MFMA, ops/s
 PEAK_FP8_FLOPS = 5.0e15
+PEAK_FP6_FLOPS = 10.1e15      # fp6 / fp4 MFMA, dense
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_FP32_VECTOR_FLOPS = 157.3e12
 PEAK_HBM_BYTES = 8.0e12       # HBM3E, bytes/s
