@@ -16,15 +16,16 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound, M = 2048: 1342/1883 = 0.713 >= 0.65 > 759/1883 = 0.40 (g=64)
+    # compute-bound, M = 2048: 1399/2052 = 0.682 >= 0.65 > 761/2052 = 0.371 (g=64)
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # M = 8192: mixed 1570/2212 = 0.710 qualifies at 0.70 (g=128, 0.656, does
-    # not); at 0.75 only g=256 (1663/2212 = 0.752) and coarser do; at 0.8 only g=K
+    # M = 8192: mixed 1741/2432 = 0.716 qualifies at 0.70 (g=128, 0.667, does
+    # not); at 0.74 only g=256 (1807/2432 = 0.743) and coarser do; at 0.8 only g=K
     assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.74) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.80) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 
