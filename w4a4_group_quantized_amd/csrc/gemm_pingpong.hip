@@ -20,12 +20,12 @@
 //   waves 0..3, stage t:  | matrix(t)    | rescale(t)  |
 //   waves 4..7, stage t:  | rescale(t-1) | matrix(t)   |
 //
-// The matrix phase holds everything that needs LDS or the matrix unit: the
-// fragment reads and the 16 int8 MFMAs of the stage, the copy of stage t+1
-// (16-byte global loads two stages ahead, widened to int8 and stored to LDS,
-// interleaved with the MFMAs by the scheduler), and the scale products
-// S = s_a * s_w of the 4 tiles.  The vector phase is only the convert + fma
-// of the 64 outputs per lane, from registers.
+// The matrix phase holds the fragment reads and the 16 int8 MFMAs of the
+// stage, most of the copy of stage t+1 (16-byte global loads two stages
+// ahead, widened to int8 and stored to LDS), and the scale products
+// S = s_a * s_w of the 4 tiles.  The vector phase is the convert + fma of
+// the 64 outputs per lane, from registers, and the last of the thread's
+// three copy chunks (the matrix phase is the longer one).
 //
 // LDS: A and B stages (int8, widened from nibbles in the global -> LDS copy,
 // 144-byte rows so that 16 consecutive rows hit every bank once) and the
@@ -274,11 +274,15 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         if (EARLY || !MIXED)
             rs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g, 0));
     };
-    auto store_stage = [&](int buf, int set) {
+    // (chunks j0 .. j1-1 of the thread's share, default all of them, and the
+    // scale row if `scale`)
+    auto store_stage = [&](int buf, int set, int j0 = 0, int j1 = 1 << 30, bool scale = true) {
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) anchor(rq[set][j]);   // widen in this phase
+        for (int j = 0; j < NCH; ++j)
+            if (j >= j0 && j < j1) anchor(rq[set][j]);   // widen in this phase
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
+            if (j < j0 || j >= j1) continue;
             uint8_t* base = chunk_is_b(j) ? sh.b[buf] : sh.a[buf];
             if (F8) {
                 *reinterpret_cast<uint4*>(base + loff[j]) = rq[set][j];
@@ -287,6 +291,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 *reinterpret_cast<uint4*>(base + loff[j] + 16) = widen_hi(rq[set][j]);
             }
         }
+        if (!scale) return;
         if (EARLY) {
             // A scale of row ht, with the 2^-8 of the widened operands folded
             // in (FP8 codes are the values themselves)
@@ -561,22 +566,26 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             if (ends) rescale(grp);
         } else if (EARLY) {
             // groups of one stage, ping-pong.  Phase 1: matrix work of stage
-            // t, copy of stage t+1
+            // t, most of the copy of stage t+1.  Phase 2: rescale of stage
+            // t's group and the rest of the copy (the matrix phase is the
+            // longer one: one of the thread's three chunks is stored here)
             load_stage(t + 2, h);
             mma_stage(h, true, true);
-            store_stage(h ^ 1, h ^ 1);
+            store_stage(h ^ 1, h ^ 1, 0, NCH - 1, true);
             lds_barrier();
-            // phase 2: rescale of stage t's group
             rescale(t);
+            store_stage(h ^ 1, h ^ 1, NCH - 1, NCH, false);
             lds_barrier();
         } else {
-            // phase 1: rescale of stage t-1's group
+            // phase 1: rescale of stage t-1's group, the last chunk of the
+            // copy of stage t+1 (its buffer was last read in stage t-1);
+            // phase 2: matrix work of stage t, the rest of the copy
             if (t > 0) rescale(t - 1);
+            store_stage(h ^ 1, h ^ 1, NCH - 1, NCH, false);
             lds_barrier();
-            // phase 2: matrix work of stage t, copy of stage t+1
             load_stage(t + 2, h);
             mma_stage(h, true, true);
-            store_stage(h ^ 1, h ^ 1);
+            store_stage(h ^ 1, h ^ 1, 0, NCH - 1, true);
             lds_barrier();
         }
         }
