@@ -25,7 +25,8 @@
 // ahead, widened to int8 and stored to LDS), and the scale products
 // S = s_a * s_w of the 4 tiles.  The vector phase is the convert + fma of
 // the 64 outputs per lane, from registers, and the last of the thread's
-// three copy chunks (the matrix phase is the longer one).
+// three copy chunks (the matrix phase is the longer one; in mixed mode, with
+// its larger rescale, the whole copy stays in the matrix phase).
 //
 // LDS: A and B stages (int8, widened from nibbles in the global -> LDS copy,
 // 144-byte rows so that 16 consecutive rows hit every bank once) and the
@@ -211,6 +212,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     constexpr int ROWB_S = F8 ? 128 : ROWB;      // operand bytes per row per stage
     constexpr int CPR = ROWB_S / 16;             // 16-byte chunks per row per stage
     constexpr int NCH = 3 * CPR / 4;             // chunks per thread per stage
+    constexpr int SPLIT = MIXED ? NCH : NCH - 1;  // chunks stored in the matrix phase (groups of one stage)
     constexpr int NSET = F8 ? 1 : 2;             // register sets of the copy
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -568,24 +570,25 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             // groups of one stage, ping-pong.  Phase 1: matrix work of stage
             // t, most of the copy of stage t+1.  Phase 2: rescale of stage
             // t's group and the rest of the copy (the matrix phase is the
-            // longer one: one of the thread's three chunks is stored here)
+            // longer one: one of the thread's three chunks is stored here;
+            // not in mixed mode, whose rescale is the longer)
             load_stage(t + 2, h);
             mma_stage(h, true, true);
-            store_stage(h ^ 1, h ^ 1, 0, NCH - 1, true);
+            store_stage(h ^ 1, h ^ 1, 0, SPLIT, true);
             lds_barrier();
             rescale(t);
-            store_stage(h ^ 1, h ^ 1, NCH - 1, NCH, false);
+            store_stage(h ^ 1, h ^ 1, SPLIT, NCH, false);
             lds_barrier();
         } else {
-            // phase 1: rescale of stage t-1's group, the last chunk of the
-            // copy of stage t+1 (its buffer was last read in stage t-1);
-            // phase 2: matrix work of stage t, the rest of the copy
+            // phase 1: rescale of stage t-1's group, the vector phase's part
+            // of the copy of stage t+1 (its buffer was last read in stage
+            // t-1); phase 2: matrix work of stage t, the rest of the copy
             if (t > 0) rescale(t - 1);
-            store_stage(h ^ 1, h ^ 1, NCH - 1, NCH, false);
+            store_stage(h ^ 1, h ^ 1, SPLIT, NCH, false);
             lds_barrier();
             load_stage(t + 2, h);
             mma_stage(h, true, true);
-            store_stage(h ^ 1, h ^ 1, 0, NCH - 1, true);
+            store_stage(h ^ 1, h ^ 1, 0, SPLIT, true);
             lds_barrier();
         }
         }
