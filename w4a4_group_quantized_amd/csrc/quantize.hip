@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256) void quantize_groups_kernel(const half8* __res
 // block at + q * 1024 + i * 16.  A tile's chunk q of 64 rows is then one
 // contiguous KB: one direct-to-LDS load of the GEMM.
 //
-// One thread per (row, half group): 64 codes (eight 16-byte loads), the two
-// halves of a group in neighbouring lanes, 48 bytes out (chunks 3h .. 3h+2).
+// One thread per (row, group): 128 codes (sixteen 16-byte loads), 96 bytes
+// out.  The 64 lanes of a wave are the 64 rows of one block and group, so
+// each of the thread's six chunk stores is one contiguous KB of the tile.
 __device__ inline uint32_t f6_field(uint32_t word, int i)
 {
     const int c = (int)(word << (28 - 4 * i)) >> 28;
@@ -80,46 +81,43 @@ __global__ __launch_bounds__(256) void quantize_f6_kernel(const half8* __restric
                                                           float* __restrict__ s)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t hpr = K / 64;                    // half groups per row
-    const int64_t r = t / hpr, hg = t - r * hpr;
+    const int64_t G = K / 128;
+    const int64_t rest = t >> 6, j = rest % G, rb = rest / G;
+    const int64_t r = rb * 64 + (t & 63);
     const bool in = t < n_threads;
     const bool live = in && r < rows;              // padding rows of the last block: zeros
-    half8 h[8];
+    half8 h[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = half8{};
+    for (int i = 0; i < 16; ++i) h[i] = half8{};
     if (live) {
-        const half8* xr = x + r * (K / 8) + 8 * hg;
+        const half8* xr = x + r * (K / 8) + 16 * j;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = xr[i];
+        for (int i = 0; i < 16; ++i) h[i] = xr[i];
     }
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, absmax8(h[i]));
-    // the other half of the group: the neighbouring lane (K / 64 is even)
-    m = fmaxf(m, dpp_move<0xB1>(m));
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, absmax8(h[i]));
     const float scale = m / 7.0f;
     const bool nz = m != 0.0f;
     if (in) {
-        uint32_t o[12];
+        uint32_t o[24];
 #pragma unroll
-        for (int i = 0; i < 12; ++i) o[i] = 0;
+        for (int i = 0; i < 24; ++i) o[i] = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
             const uint32_t w = quantize8(h[i], scale, nz && live);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t f = f6_field(w, k);
-                const int b = 6 * (8 * i + k);     // bit position in the 48 bytes
+                const int b = 6 * (8 * i + k);     // bit position in the 96 bytes
                 o[b / 32] |= f << (b % 32);
                 if (b % 32 > 26) o[b / 32 + 1] |= f >> (32 - b % 32);
             }
         }
-        const int64_t G = K / 128, j = hg >> 1, half = hg & 1;
-        uint4* tile = q + ((r >> 6) * G + j) * 6 * 64 + (r & 63);
+        uint4* tile = q + (rb * G + j) * 6 * 64 + (t & 63);
 #pragma unroll
-        for (int c = 0; c < 3; ++c)
-            tile[(3 * half + c) * 64] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-        if (live && half == 0) s[r * G + j] = nz ? scale : 0.0f;
+        for (int c = 0; c < 6; ++c) tile[c * 64] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+        if (live) s[r * G + j] = nz ? scale : 0.0f;
     }
 }
 
@@ -183,7 +181,7 @@ namespace apex4 {
 hipError_t launch_quantize_f6(const void* x_f16, int64_t rows, int64_t K, void* q6, float* s, hipStream_t stream)
 {
     // rows padded to whole blocks of 64
-    const int64_t n_threads = (rows + 63) / 64 * 64 * (K / 64);
+    const int64_t n_threads = (rows + 63) / 64 * 64 * (K / 128);
     const unsigned blocks = (unsigned)((n_threads + 255) / 256);
     quantize_f6_kernel<<<blocks, 256, 0, stream>>>(static_cast<const half8*>(x_f16), rows, K, n_threads,
                                                    static_cast<uint4*>(q6), s);
