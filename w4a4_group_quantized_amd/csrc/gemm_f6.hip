@@ -161,6 +161,12 @@ __device__ __forceinline__ void f6_body(const F6Args& a, StageBuf& b0, StageBuf&
     if (a.part) {
         kpart = lin / a.ntail;
         lin -= kpart * a.ntail;
+    } else {
+        // XCD-aware order, as in the nibble ping-pong kernel: the chip deals
+        // workgroup b to XCD b mod 8 (each with its own L2), which then walks
+        // a contiguous range of tile ids (bands of 4 row blocks)
+        const int per = (int)gridDim.x >> 3;
+        if (lin < per * 8) lin = (lin & 7) * per + (lin >> 3);
     }
     int by, bx;
     tile_coords(a, a.tile0 + lin, by, bx);
@@ -469,7 +475,7 @@ hipError_t launch_gemm_f6(const GemmProblem& p, hipStream_t stream)
     t.prows = p.prows;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
-    t.group_m = t.tiles_m < 16 ? t.tiles_m : 16;
+    t.group_m = t.tiles_m < 4 ? t.tiles_m : 4;   // one XCD's 32 tiles in flight: 4 x 8 blocks
     t.nparts = 1;
     // the partial last round as K parts: the split (and workspace) of the
     // nibble kernels for groups of 128

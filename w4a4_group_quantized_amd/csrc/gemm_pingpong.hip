@@ -96,11 +96,13 @@ struct PPArgs {
     int32_t* psum;
     PsumRows prows;
     // Tiles: BM x BN blocks of Y, numbered in bands of group_m row blocks:
-    // down a column of the band, then the next column (so that the
-    // workgroups in flight share few A and B blocks: fewer re-reads of B
-    // from HBM than in row-major order); workgroup b of a launch takes tile
-    // tile0 + b (full K, the epilogue
-    // writes Y) or, in a K-split launch (part != null), tile tile0 + b % ntail
+    // down a column of the band, then the next column, so that the
+    // workgroups in flight share few A and B blocks.  The chip deals
+    // workgroup b to XCD b mod 8, each XCD with its own L2, so in a full-K
+    // launch of B workgroups, b (< 8 floor(B/8)) takes tile tile0 +
+    // (b mod 8) floor(B/8) + b div 8: each XCD walks a contiguous range of
+    // tile ids, its 32 workgroups in flight covering 4 row blocks x 8 column
+    // blocks (the epilogue writes Y); in a K-split launch (part != null), tile tile0 + b % ntail
     // over K part q = b / ntail of nparts (stages [q S / nparts, (q+1) S /
     // nparts) of the S = K/128), writing its fp32 sums to part[q][b % ntail]
     // ([BM][BN], before s_w in mixed mode) for the reduction kernel.
@@ -222,6 +224,10 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     if (a.part) {
         kpart = lin / a.ntail;
         lin -= kpart * a.ntail;
+    } else {
+        // XCD-aware order: XCD b mod 8 takes a contiguous range of tile ids
+        const int per = (int)gridDim.x >> 3;
+        if (lin < per * 8) lin = (lin & 7) * per + (lin >> 3);
     }
     const int tile = a.tile0 + lin;
     int by, bx;
@@ -721,7 +727,9 @@ void launch_pp_all(const PPArgs& t, const PingpongSplit& sp, hipStream_t stream)
 // Row blocks per band of the tile order: 16 (a round of 256 workgroups then
 // covers 16 x 16 tiles: at K = 8192 their A and B blocks are 24 MB, against
 // 129 MB for one row block and 256 column blocks in row-major order).
-int tile_band_rows(int tiles_m) { return tiles_m < 16 ? tiles_m : 16; }
+// row blocks per band: 32 consecutive tiles (one XCD's workgroups in flight)
+// cover 4 row blocks x 8 column blocks
+int tile_band_rows(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 
 int cu_count()
 {
