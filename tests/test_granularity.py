@@ -16,16 +16,18 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound, M = 2048: 1399/2052 = 0.682 >= 0.65 > 761/2052 = 0.371 (g=64)
+    # compute-bound, M = 2048: 1411/1997 = 0.707 >= 0.65 > 764/1997 = 0.383 (g=64)
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # M = 8192: mixed 1741/2432 = 0.716 qualifies at 0.70 (g=128, 0.667, does
-    # not); at 0.74 only g=256 (1807/2432 = 0.743) and coarser do; at 0.8 only g=K
-    assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.74) == (256, 256)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
+    # M = 8192: g=128 1646/2344 = 0.702 qualifies at 0.70; at 0.72 mixed
+    # (1737/2344 = 0.741) is the finest that does; at 0.75 only g=256
+    # (1796/2344 = 0.766) and coarser; at 0.8 only g=K
+    assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 128)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (128, 8192)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.77) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.80) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
 
@@ -43,7 +45,7 @@ def test_decode_picks_a_streaming_mode():
 
 
 def test_decode_fine_groups_only_on_a_tiny_budget():
-    # accepting 20x slower than the fastest mode admits the tiled g=32 (0.08)
+    # accepting 20x slower than the fastest mode admits the tiled g=32 (0.084)
     assert apex4.select_granularity(1, 28672, 8192, 0.05) == (32, 32)
 
 
