@@ -23,9 +23,10 @@
 // sums of the row first and rescales once; mixed mode (per-channel weight
 // scales) rescales with s_a and applies s_w to the row sum.
 //
-// The activation rows and their scales are copied to LDS once per workgroup
-// (the first weight loads are issued before that copy, so it overlaps their
-// latency).  Per weight word the lane issues M dot8 and reads M activation
+// The activation rows and their scales are copied to LDS once per workgroup;
+// their loads go out first and the first weight loads right after, so the
+// wait for the copy leaves the weights in flight (issued the other way
+// round, that wait also waited for the weights' HBM latency).  Per weight word the lane issues M dot8 and reads M activation
 // words from LDS, so the kernel stays at the weight-streaming rate only for
 // a few rows: from 3 rows on the LDS-streaming MFMA kernel is faster, and the
 // dispatch sends only 1 or 2 rows here.  Lane l reads the four 16-byte quads
@@ -123,11 +124,8 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
         ws[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                  rS, live ? (int)(((uint32_t)n * a.Gw + j) * 4) : (int)OOB, 0, 0));
     };
-    // (the fused prologue's activation loads go out first, ahead of the weights)
-    if constexpr (!FUSED) {
-#pragma unroll
-        for (int k = 0; k < PF - 1; ++k) issue(k, k);
-    }
+    // (the activation loads go out first, ahead of the weights: their wait
+    // then leaves the weight loads in flight)
 
     // --- activation rows (rows past M zero) and their scales into LDS ---
     float* lsa = reinterpret_cast<float*>(lds + MR * rowbytes);
@@ -166,11 +164,30 @@ __global__ __launch_bounds__(THREADS) void gemm_gemv_kernel(GemvArgs a)
             }
         }
     } else {
+        // the first NA chunks of this thread in registers, then the first
+        // weight loads, then the stores (and any chunks beyond NA)
+        constexpr int NA = 4;
         const uint4* src = reinterpret_cast<const uint4*>(a.qa);
         uint4* dst = reinterpret_cast<uint4*>(lds);
         const int nq = MR * (int)rowbytes / 16, live_q = a.lds_qa / 16;
-        for (int i = tid; i < nq; i += THREADS) dst[i] = i < live_q ? src[i] : make_uint4(0, 0, 0, 0);
-        for (int i = tid; i < MR * a.Ga; i += THREADS) lsa[i] = i < a.M * a.Ga ? a.sa[i] : 0.0f;
+        uint4 av[NA];
+        float sv = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NA; ++c) {
+            const int i = tid + c * THREADS;
+            av[c] = i < live_q ? src[i] : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < MR * a.Ga) sv = tid < a.M * a.Ga ? a.sa[tid] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < PF - 1; ++k) issue(k, k);
+#pragma unroll
+        for (int c = 0; c < NA; ++c) {
+            const int i = tid + c * THREADS;
+            if (i < nq) dst[i] = av[c];
+        }
+        if (tid < MR * a.Ga) lsa[tid] = sv;
+        for (int i = tid + NA * THREADS; i < nq; i += THREADS) dst[i] = i < live_q ? src[i] : make_uint4(0, 0, 0, 0);
+        for (int i = tid + THREADS; i < MR * a.Ga; i += THREADS) lsa[i] = i < a.M * a.Ga ? a.sa[i] : 0.0f;
     }
     if constexpr (FUSED) {
 #pragma unroll
