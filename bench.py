@@ -61,6 +61,8 @@ WORKLOADS = {
                  "student_t"),
     "sweep-mixed": ("granularity sweep, mixed (per-channel weights, g=128 activations)", 8192,
                     [(8192, 28672)], 128, 8192, "student_t"),
+    "sweep-mixed64": ("granularity sweep, mixed (per-channel weights, g=64 activations)", 8192,
+                      [(8192, 28672)], 64, 8192, "student_t"),
 }
 # The same layer sets on FP8-coded operands (apex4_quantize_f8, apex4_gemm_w4a4_f8):
 # name -> the INT4 workload it mirrors
@@ -117,7 +119,7 @@ def parse():
                          "(M:K:N,M:K:N,...; back-to-back launches, weights cycled past the "
                          "last-level cache) and print one JSON line of rates per shape: the "
                          "measurements behind apex4_select_granularity")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8,llama2-70b-prefill-f6,sweep-g32,sweep-g64",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 
@@ -195,8 +197,22 @@ def cpu_baseline(layers, M, ga, gw, act, rows_per_layer, target_s=12.0):
 
 
 CSRC = os.path.join(ROOT, "w4a4_group_quantized_amd", "csrc")
-# sources every GEMM launch goes through (kernel choice, shared declarations)
+# sources every GEMM launch goes through (kernel choice, shared declarations);
+# the files that define the kernels' shape predicates (`..._supports`) are
+# added too, since a change in any of them can move a workload to another kernel
 COMMON_SOURCES = ("gemm_dispatch.cpp", "internal.h")
+
+
+def dispatch_sources():
+    """The csrc files that define a kernel-choice predicate (bool ..._supports(...))."""
+    import re
+    out = []
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp")):
+            with open(os.path.join(CSRC, name)) as f:
+                if re.search(r"\bbool\s+\w+_supports\s*\(", f.read()):
+                    out.append(name)
+    return out
 
 
 def kernel_sources_sha256(files):
@@ -218,7 +234,7 @@ def kernel_source_files(kernel_names):
     idents = set()
     for k in kernel_names:
         idents.update(re.findall(r"(\w+_kernel)\b", k))
-    files = set(COMMON_SOURCES)
+    files = set(COMMON_SOURCES) | set(dispatch_sources())
     for name in sorted(os.listdir(CSRC)):
         if not name.endswith((".hip", ".cpp")):
             continue

@@ -305,10 +305,10 @@ apex4_status apex4_gemm_w4a4_f6(const void* qa6, const float* s_a, const void* q
  *   - otherwise the tiled kernels, which work in whole 256-row tiles:
  *     max(bytes / 5.0e12 B/s, 2*M'*N*K / rate) with M' = M rounded up to a
  *     multiple of 256 and the rate interpolated from the measured TOPS at
- *     M' = 256, 2048, 4096, 8192 (g = 32: 432..580, 64: 660..843, 128:
- *     1333..1452, mixed: 1292..1570, 256: 1412..1663, K: 1838..2212).
+ *     M' = 256, 2048, 4096, 8192 (g = 32: 497..603, 64: 1040..1249, 128:
+ *     1355..1627, mixed: 1410..1729, 256: 1516..1799, K: 1886..2361).
  * Groups of 32 and 64 have no weight-streaming kernel: at decode sizes they
- * run on mostly empty 256-row tiles and are modelled (and measured) ten or
+ * run on mostly empty 256-row tiles and are modelled (and measured) five or
  * more times slower.  The finest mode whose modelled speed is at least
  * min_rel_speed times the fastest mode's is returned.  Modes whose groups do
  * not divide K are skipped, and so is one group over K for K >= 2^17 (see

@@ -201,6 +201,20 @@ def test_gemm_decode_rows(dev, M, ga, gw, K):
     run_case(dev, x, w, ga, gw, want_p=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 300, 1024), (260, 130, 2560), (513, 257, 3328), (65, 1000, 1152),
+                                   (1024, 512, 4096)])
+@pytest.mark.parametrize("ga,gw", [(64, 64), (64, "K"), (32, 32)])
+def test_gemm_groups_within_a_stage(dev, M, N, K, ga, gw):
+    """Groups of 64 and 32 on the ping-pong tiled kernel: two or four groups
+    per 128-value stage, each with its own matrix phase, scale products and
+    rescale; 9, 20, 26 and 32 stages (odd and even loop ends), ragged M and
+    N, a single mostly empty row tile (65 rows); also mixed mode with
+    activation groups of 64 (per-channel weight scales)."""
+    gw = K if gw == "K" else gw
+    x, w = inputs.problem(M, N, K, seed=43 + M, act="outlier")
+    run_case(dev, x, w, ga, gw, want_p=True)
+
+
 @pytest.mark.parametrize("M,N,K", [(300, 300, 1024), (260, 130, 2560), (513, 257, 3328)])
 @pytest.mark.parametrize("ga,gw", [(256, 256), (256, "K")])
 def test_gemm_groups_of_two_stages(dev, M, N, K, ga, gw):
@@ -232,7 +246,7 @@ def test_gemm_decode_many_blocks(dev, M, N, K, ga, gw):
 
 
 @pytest.mark.parametrize("M,g", [(1, 128), (2, 256), (8, 128), (13, "K"), (40, 128), (40, 256), (64, "K"),
-                                 (300, 128), (300, 256), (300, "K"), (300, 32), (520, 64)])
+                                 (300, 128), (300, 256), (300, "K"), (300, 32), (520, 64), (17, 64)])
 def test_gemm_debug_rows(dev, M, g):
     """apex4_gemm_w4a4_debug keeps the group sums of every p_step-th row from
     p_row0: each kernel (row-streaming, LDS-streaming, K-outer, skinny,
@@ -344,7 +358,10 @@ def test_full_granularity_sweep(dev, ga, gw):
 
 @pytest.mark.parametrize("M,N,K,ga,gw", [(300, 16640, 512, 128, 128), (257, 16512, 1152, 128, 128),
                                          (300, 16640, 1024, 128, 1024), (130, 1000, 4096, 128, 128),
-                                         (300, 4096, 1024, 128, 128), (65, 640, 2048, 128, 2048)])
+                                         (300, 4096, 1024, 128, 128), (65, 640, 2048, 128, 2048),
+                                         (300, 16640, 512, 64, 64), (257, 16512, 1152, 64, 64),
+                                         (300, 16640, 1024, 64, 1024), (300, 16640, 512, 32, 32),
+                                         (257, 16512, 1152, 32, 32)])
 def test_gemm_split_last_round(dev, M, N, K, ga, gw):
     """Shapes whose last round of 256x128 output tiles (the only one, for few
     tiles) fills at most half the GPU's compute units: those tiles run as 2 to

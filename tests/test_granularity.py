@@ -16,15 +16,26 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound, M = 2048: 1411/1997 = 0.707 >= 0.65 > 764/1997 = 0.383 (g=64)
+    # compute-bound, M = 2048: 1394/1991 = 0.700 >= 0.65 > 1072/1991 = 0.538 (g=64)
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
+def test_prefill_picks_g64_at_half_speed():
+    # groups of 64 on the ping-pong kernel: 1072/1991 = 0.538 (M = 2048) and
+    # 1249/2361 = 0.529 (M = 8192) qualify at 0.5, g=32 (546/1991 = 0.274,
+    # 602/2361 = 0.255) does not
+    assert apex4.select_granularity(2048, 12288, 4096, 0.5) == (64, 64)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.5) == (64, 64)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.55) == (128, 128)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.2) == (32, 32)
+
+
 def test_prefill_tighter_budgets_coarsen():
-    # M = 8192: g=128 1646/2344 = 0.702 qualifies at 0.70; at 0.72 mixed
-    # (1737/2344 = 0.741) is the finest that does; at 0.75 only g=256
-    # (1796/2344 = 0.766) and coarser; at 0.8 only g=K
-    assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 128)
+    # M = 8192: g=128 1627/2361 = 0.689 qualifies at 0.68; at 0.70 and 0.72
+    # mixed (1729/2361 = 0.732) is the finest that does; at 0.75 only g=256
+    # (1791/2361 = 0.759) and coarser; at 0.8 only g=K
+    assert apex4.select_granularity(8192, 28672, 8192, 0.68) == (128, 128)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (128, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
     assert apex4.select_granularity(8192, 28672, 8192, 0.77) == (8192, 8192)
@@ -35,7 +46,7 @@ def test_prefill_tighter_budgets_coarsen():
 def test_decode_picks_a_streaming_mode():
     # M = 1, N = 28672, K = 8192: the streaming kernels read ~118-125 MB at
     # ~5.2 TB/s (mixed mode fastest, 22.4 us; g=128 23.6 us, 0.95 of it); g=32
-    # and g=64 run on 256-row tiles (~180-280 us)
+    # and g=64 run on 256-row tiles (~240 and ~115 us)
     assert apex4.select_granularity(1, 28672, 8192, 0.75) == (128, 128)
     assert apex4.select_granularity(1, 28672, 8192, 0.96) == (128, 8192)
     for M in (1, 4, 16, 64):
@@ -45,8 +56,11 @@ def test_decode_picks_a_streaming_mode():
 
 
 def test_decode_fine_groups_only_on_a_tiny_budget():
-    # accepting 20x slower than the fastest mode admits the tiled g=32 (0.084)
+    # accepting 11x slower than the fastest mode admits g=32 on 256-row tiles
+    # (0.093); 5x slower g=64 (0.19)
     assert apex4.select_granularity(1, 28672, 8192, 0.05) == (32, 32)
+    assert apex4.select_granularity(1, 28672, 8192, 0.09) == (32, 32)
+    assert apex4.select_granularity(1, 28672, 8192, 0.10) == (64, 64)
 
 
 def test_one_group_over_large_k_not_offered():

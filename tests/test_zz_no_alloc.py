@@ -42,6 +42,7 @@ PAIRS = [
     ((300, 16640, 1024, 128, 128), (130, 1000, 4096, 128, 128)),
     ((64, 8192, 8192, 128, 128), (17, 8192, 4096, 128, 128)),
     ((300, 16640, 1024, 128, 1024), (65, 640, 2048, 128, 2048)),
+    ((300, 16640, 512, 64, 64), (257, 16512, 1152, 64, 64)),
 ]
 
 

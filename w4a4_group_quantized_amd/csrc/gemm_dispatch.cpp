@@ -4,8 +4,8 @@
 // with K outside the column blocks (the skinny kernel, feeding the matrix
 // units from global memory, covers the group modes those lack).  Otherwise the call is
 // compute-bound and one of the tiled kernels runs (the ping-pong one for
-// groups of 128 or one group over K, the step-major one for the other group
-// sizes).
+// groups of 64, 128, 256 or one group over K, the step-major one for groups
+// of 32 and for mixed mode with activation groups of 32 or 64).
 #include "internal.h"
 
 namespace apex4 {

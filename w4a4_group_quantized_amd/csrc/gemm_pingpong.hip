@@ -1,5 +1,6 @@
 // W4A4 GEMM with per-group dequantization on gfx950: the ping-pong tiled
-// kernel for compute-bound calls with groups of 128 (or one group over K).
+// kernel for compute-bound calls with groups of 32, 64, 128 or 256 (or one
+// group over K).
 //
 // The computation is the APEX4 page's (Abstract): INT4 x INT4 products summed
 // exactly per K-group on the matrix units, every group's integer sum rescaled
@@ -42,7 +43,19 @@
 // is rescaled once; with no rescale to overlap, both wave groups then run the
 // matrix work of every stage together (one barrier per stage: the ping-pong
 // offset would only leave each SIMD's matrix unit with one wave).  Mixed mode (per-channel weight scales, activation groups
-// of 128) rescales with s_a alone and applies s_w in the epilogue.
+// of 64, 128 or 256) rescales with s_a alone and applies s_w in the epilogue.
+//
+// Groups of 64 and 32.  A 128-value stage holds two (four) groups, so the
+// ping-pong runs per group: four (eight) phases per stage, in each a wave
+// either issues one group's 8 (4) MFMAs and its scale products, or rescales
+// the group it finished before.  The copy of the next stage is stored in the
+// stage's matrix phases, and its scale rows hold every group of the stage
+// (156 KB of LDS in all).  Several groups' int32 sums would not fit in the
+// registers beside the accumulators; one group per phase needs no more than
+// groups of 128 do.  At groups of 32 the four groups' scale rows fit in LDS
+// only as single 16-byte entries: their products come from the K = 8
+// split-operand MFMA (v_mfma_f32_32x32x8_bf16), which takes slots 0..3 from
+// lanes 0..31 and 4..7 from lanes 32..63, so no zero half is stored.
 //
 // FP8-coded operands (apex4_gemm_w4a4_f8).  The same kernel with each code
 // stored as its exact E4M3 byte: the copy stores the bytes as they come (no
@@ -70,6 +83,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256;
@@ -89,7 +103,7 @@ struct PPArgs {
     const float* sw;
     int M, N, K;
     int Ga, Gw;        // scale columns per row: K/ga, K/gw
-    int spg;           // stages per group: gs / 128 (1, or all of K)
+    int spg;           // stages per group: gs / 128 (1, 2, or all of K; -1: groups of 64, -2: of 32)
     int G;             // K / gs
     _Float16* y16;
     float* y32;
@@ -175,18 +189,27 @@ __device__ inline void anchor(uint4& x)
 
 __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// LDS of one workgroup
+// LDS of one workgroup (NG: groups per stage, 2 for groups of 64, 4 for
+// groups of 32; HV: 16-byte halves per scale entry, 1 where the scale
+// products use the K = 8 split-operand MFMA, which needs no zero half)
+template <int NG, int HV>
 struct PPShared {
     uint8_t a[2][A_BYTES];
     uint8_t b[2][B_BYTES];
-    // Scale operands, per stage buffer: two 16-byte halves per tile row, half
+    // Scale operands, per stage buffer and group: two 16-byte halves per tile row, half
     // 0 holding the bf16 pieces in slots 0..5 and zeros in 6..7, half 1 zeros
     // (lanes 32..63 of the split-operand MFMA read it); stored half-major, so
     // that 8 consecutive rows' reads of one half are 128 contiguous bytes (as
     // 32-byte rows they were 2-way bank conflicted).  In mixed mode ta holds
     // fp32 2^-8 s_a in its first BM dwords.
-    uint4 ta[2][2][BM];
-    uint4 tb[2][2][BN];
+    uint4 ta[2][NG][HV][BM];
+    uint4 tb[2][NG][HV][BN];
+};
+
+// groups per stage and scale-row halves of a stages-per-group mode
+template <int SPG> struct PPMode {
+    static constexpr int NG = SPG == -2 ? 4 : SPG == -1 ? 2 : 1;
+    static constexpr int HV = SPG == -2 ? 1 : 2;
 };
 
 // Orders this wave's LDS accesses around the workgroup barrier (LDS only:
@@ -201,15 +224,19 @@ __device__ inline void lds_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// SPG: stages per group, 1 (g = 128), 2 (g = 256) or 0 (one group, g = K).
+// SPG: stages per group, 1 (g = 128), 2 (g = 256) or 0 (one group, g = K);
+// -1: groups of 64, two per stage; -2: groups of 32, four per stage (GN below).
 // EARLY: this wave belongs to waves 0..3.
 // F8: FP8-coded operands (one byte per code, the codes' exact E4M3 values):
 // a stage of 128 codes is 128 bytes per row, copied in 6 chunks per thread
 // through one register set (stored before the next stage's loads are
 // issued), two 64-code K-steps of the FP8 MFMA.
 template <bool MIXED, bool DEBUG_P, int SPG, bool EARLY, bool F8>
-__device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
+__device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::NG, PPMode<SPG>::HV>& sh)
 {
+    constexpr bool GN = SPG < 0;                 // groups of 64 or 32: several per stage
+    constexpr int NG = PPMode<SPG>::NG;          // groups per stage
+    constexpr int HV = PPMode<SPG>::HV;          // scale-row halves in sh.ta, sh.tb
     constexpr int KST = KSTAGE;                  // K values per stage
     constexpr int ROWB_S = F8 ? 128 : ROWB;      // operand bytes per row per stage
     constexpr int CPR = ROWB_S / 16;             // 16-byte chunks per row per stage
@@ -269,7 +296,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const uint32_t soff = !has_scale ? 0x80000000u : EARLY ? (uint32_t)ht * a.Ga * 4 : (uint32_t)ht * a.Gw * 4;
 
     uint4 rq[NSET][NCH];
-    float rs[NSET];
+    float rs[NSET][NG];
     auto load_stage = [&](int t, int set) {
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
@@ -277,10 +304,40 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 __builtin_amdgcn_raw_buffer_load_b128(chunk_is_b(j) ? rB : rA, (int)goff[j], (s0 + t) * ROWB_S, 0);
             rq[set][j] = make_uint4(v.x, v.y, v.z, v.w);
         }
-        // the scale of the group that stage t belongs to
-        const int g = (SPG == 1 ? s0 + t : SPG == 2 ? (s0 + t) >> 1 : 0) * 4;
+        // the scale of the group (groups of 64 or 32: the groups) that stage t
+        // belongs to (several groups per stage: stages past the end load the
+        // last stage's scales, which are not used)
+        const int g = (SPG == 1 ? s0 + t : SPG == 2 ? (s0 + t) >> 1 : GN ? NG * min(s0 + t, all_stages - 1) : 0) * 4;
         if (EARLY || !MIXED)
-            rs[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g, 0));
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+                rs[set][q] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(EARLY ? rSA : rSW, (int)soff, g + 4 * q, 0));
+    };
+    // the scale rows of groups q0 .. q1-1 of a stage (register set `set`)
+    // into stage buffer `buf`
+    auto store_scales = [&](int buf, int set, int q0, int q1) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            if (q < q0 || q >= q1) continue;
+            if (EARLY) {
+                // A scale of row ht, with the 2^-8 of the widened operands folded
+                // in (FP8 codes are the values themselves)
+                const float s = F8 ? rs[set][q] : rs[set][q] * 0.00390625f;
+                if (MIXED) {
+                    reinterpret_cast<float*>(sh.ta[buf][q])[ht] = s;
+                } else {
+                    uint32_t x0, x1, x2;
+                    split3(s, x0, x1, x2);
+                    // slots 0..5: x0 x0 x0 x1 x1 x2 (paired with y0 y1 y2 y0 y1 y0)
+                    sh.ta[buf][q][0][ht] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
+                }
+            } else if (has_scale) {
+                uint32_t y0, y1, y2;
+                split3(rs[set][q], y0, y1, y2);
+                sh.tb[buf][q][0][ht] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
+            }
+        }
     };
     // (chunks j0 .. j1-1 of the thread's share, default all of them, and the
     // scale row if `scale`)
@@ -299,24 +356,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 *reinterpret_cast<uint4*>(base + loff[j] + 16) = widen_hi(rq[set][j]);
             }
         }
-        if (!scale) return;
-        if (EARLY) {
-            // A scale of row ht, with the 2^-8 of the widened operands folded
-            // in (FP8 codes are the values themselves)
-            const float s = F8 ? rs[set] : rs[set] * 0.00390625f;
-            if (MIXED) {
-                reinterpret_cast<float*>(sh.ta[buf])[ht] = s;
-            } else {
-                uint32_t x0, x1, x2;
-                split3(s, x0, x1, x2);
-                // slots 0..5: x0 x0 x0 x1 x1 x2 (paired with y0 y1 y2 y0 y1 y0)
-                sh.ta[buf][0][ht] = make_uint4(x0 | (x0 << 16), x0 | (x1 << 16), x1 | (x2 << 16), 0);
-            }
-        } else if (has_scale) {
-            uint32_t y0, y1, y2;
-            split3(rs[set], y0, y1, y2);
-            sh.tb[buf][0][ht] = make_uint4(y0 | (y1 << 16), y2 | (y0 << 16), y1 | (y0 << 16), 0);
-        }
+        if (scale) store_scales(buf, set, 0, NG);
     };
 
     float acc[2][2][16];
@@ -341,23 +381,23 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     const uint32_t frag = (wm * 64 + (lane & 31)) * STRIDE + (F8 ? 32 : 16) * (lane >> 5);
     const uint32_t fragb = (wn * 64 + (lane & 31)) * STRIDE + (F8 ? 32 : 16) * (lane >> 5);
     const int trow = lane & 31, thalf = lane >> 5;
-    // The scale products S of the 4 tiles for the group of stage buffer `buf`,
+    // The scale products S of the 4 tiles for group q of stage buffer `buf`,
     // on the matrix unit, so that the vector phase has no LDS or matrix-unit
     // dependency.
-    auto scale_products = [&](int buf) {
+    auto scale_products = [&](int buf, int q = 0) {
         if (MIXED) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const float* sp = reinterpret_cast<const float*>(sh.ta[buf]) + wm * 64 + mt * 32 + 4 * thalf;
+                const float* sp = reinterpret_cast<const float*>(sh.ta[buf][q]) + wm * 64 + mt * 32 + 4 * thalf;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(sp + 8 * q);
+                for (int u = 0; u < 4; ++u) {
+                    const float4 v = *reinterpret_cast<const float4*>(sp + 8 * u);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
-                        S[mt][nt][4 * q + 0] = v.x;
-                        S[mt][nt][4 * q + 1] = v.y;
-                        S[mt][nt][4 * q + 2] = v.z;
-                        S[mt][nt][4 * q + 3] = v.w;
+                        S[mt][nt][4 * u + 0] = v.x;
+                        S[mt][nt][4 * u + 1] = v.y;
+                        S[mt][nt][4 * u + 2] = v.z;
+                        S[mt][nt][4 * u + 3] = v.w;
                     }
                 }
             }
@@ -365,14 +405,35 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
             v8bf opa[2], opb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                opa[i] = __builtin_bit_cast(v8bf, sh.ta[buf][thalf][wm * 64 + i * 32 + trow]);
-                opb[i] = __builtin_bit_cast(v8bf, sh.tb[buf][thalf][wn * 64 + i * 32 + trow]);
+                if constexpr (HV == 2) {
+                    opa[i] = __builtin_bit_cast(v8bf, sh.ta[buf][q][thalf][wm * 64 + i * 32 + trow]);
+                    opb[i] = __builtin_bit_cast(v8bf, sh.tb[buf][q][thalf][wn * 64 + i * 32 + trow]);
+                }
             }
+            if constexpr (HV == 2) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[mt], opb[nt], v16f{}, 0, 0, 0);
+                    for (int nt = 0; nt < 2; ++nt)
+                        S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[mt], opb[nt], v16f{}, 0, 0, 0);
+            } else {
+                // one 16-byte entry per scale: the K = 8 split-operand MFMA,
+                // lanes 0..31 taking slots 0..3 and lanes 32..63 slots 4..7
+                // (two of them zero), so no zero half is needed
+                v4s oa[2], ob[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    oa[i] = __builtin_bit_cast(
+                        v4s, reinterpret_cast<const uint2*>(&sh.ta[buf][q][0][wm * 64 + i * 32 + trow])[thalf]);
+                    ob[i] = __builtin_bit_cast(
+                        v4s, reinterpret_cast<const uint2*>(&sh.tb[buf][q][0][wn * 64 + i * 32 + trow])[thalf]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        S[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(oa[mt], ob[nt], v16f{}, 0, 0, 0);
+            }
         }
     };
     // Matrix phase of stage buffer `buf`: the 16 int8 MFMAs, K-step-major so
@@ -446,6 +507,31 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
         }
         if (ends) scale_products(buf);
     };
+    // Several groups per stage: the matrix phase of group q of stage buffer
+    // `buf`, its K-steps (groups of 64: 2q and 2q+1, 8 MFMAs; groups of 32:
+    // q, 4 MFMAs) from zero, then its scale products.
+    auto mma_group = [&](int buf, int q) {
+        constexpr int KS = 4 / NG;   // 32-value K-steps per group
+        const uint8_t* la = sh.a[buf] + frag + 32 * KS * q;
+        const uint8_t* lb = sh.b[buf] + fragb + 32 * KS * q;
+        v4i fa[2][KS], fb[2][KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i][s] = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 32 * s);
+                fb[i][s] = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 32 * s);
+            }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    P[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[mt][s], fb[nt][s],
+                                                                      s == 0 ? v16i{} : P[mt][nt], 0, 0, 0);
+        scale_products(buf, q);
+    };
 
     // Vector phase: acc += S (.) P for the finished group j (counted from
     // this workgroup's first stage s0; the debug sums take the index over all
@@ -474,7 +560,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                     acc[mt][nt][r] = fmaf(S[mt][nt][r], (float)P[mt][nt][r], acc[mt][nt][r]);
                 if (DEBUG_P) {
                     const int n = n0 + wn * 64 + nt * 32 + (lane & 31);
-                    const int jg = SPG == 0 ? j : s0 / SPG + j;
+                    const int jg = SPG == 0 ? j : GN ? NG * s0 + j : s0 / SPG + j;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = m0 + wm * 64 + mt * 32 + acc_row(r, lane);
@@ -495,9 +581,13 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     // --- prologue: the zero halves of the scale rows, stages 0 and 1 in
     // flight, stage 0 into buffer 0 ---
     if (!MIXED) {
-        for (int i = tid; i < 2 * (BM + BN); i += THREADS) {
-            if (i < 2 * BM) sh.ta[i / BM][1][i % BM] = make_uint4(0, 0, 0, 0);
-            else sh.tb[(i - 2 * BM) / BN][1][(i - 2 * BM) % BN] = make_uint4(0, 0, 0, 0);
+        if constexpr (HV == 2) {
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+                for (int i = tid; i < 2 * (BM + BN); i += THREADS) {
+                    if (i < 2 * BM) sh.ta[i / BM][q][HV - 1][i % BM] = make_uint4(0, 0, 0, 0);
+                    else sh.tb[(i - 2 * BM) / BN][q][HV - 1][(i - 2 * BM) % BN] = make_uint4(0, 0, 0, 0);
+                }
         }
     }
     if constexpr (F8) {
@@ -513,6 +603,73 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
 
     // Stage t uses A/B and scale buffer t&1 and register set t&1; the loop is
     // unrolled by two so that these are compile-time indices.
+    if constexpr (NG == 4) {
+        // Groups of 32, ping-pong per group: eight phases per stage, the four
+        // groups' matrix work and rescales alternating as for groups of one
+        // stage.  The copy of stage t+1 is stored in the first three matrix
+        // phases, one chunk each, and group q's scale rows in matrix phase q
+        // (its buffer was last read in the phase before this stage's first).  The
+        // buffer parity h is a template constant here (the stage body is too
+        // large for the compiler to unroll the loop below).
+        auto stage32 = [&](auto hc, int t) __attribute__((always_inline)) {
+            constexpr int h = decltype(hc)::value;
+            if (EARLY) {
+                load_stage(t + 2, h);
+                mma_group(h, 0);
+                store_stage(h ^ 1, h ^ 1, 0, 1, false);
+                store_scales(h ^ 1, h ^ 1, 0, 1);
+                lds_barrier();
+                rescale(4 * t);
+                lds_barrier();
+                mma_group(h, 1);
+                store_stage(h ^ 1, h ^ 1, 1, 2, false);
+                store_scales(h ^ 1, h ^ 1, 1, 2);
+                lds_barrier();
+                rescale(4 * t + 1);
+                lds_barrier();
+                mma_group(h, 2);
+                store_stage(h ^ 1, h ^ 1, 2, NCH, false);
+                store_scales(h ^ 1, h ^ 1, 2, 3);
+                lds_barrier();
+                rescale(4 * t + 2);
+                lds_barrier();
+                mma_group(h, 3);
+                store_scales(h ^ 1, h ^ 1, 3, 4);
+                lds_barrier();
+                rescale(4 * t + 3);
+                lds_barrier();
+            } else {
+                if (t > 0) rescale(4 * t - 1);
+                lds_barrier();
+                load_stage(t + 2, h);
+                mma_group(h, 0);
+                store_stage(h ^ 1, h ^ 1, 0, 1, false);
+                store_scales(h ^ 1, h ^ 1, 0, 1);
+                lds_barrier();
+                rescale(4 * t);
+                lds_barrier();
+                mma_group(h, 1);
+                store_stage(h ^ 1, h ^ 1, 1, 2, false);
+                store_scales(h ^ 1, h ^ 1, 1, 2);
+                lds_barrier();
+                rescale(4 * t + 1);
+                lds_barrier();
+                mma_group(h, 2);
+                store_stage(h ^ 1, h ^ 1, 2, NCH, false);
+                store_scales(h ^ 1, h ^ 1, 2, 3);
+                lds_barrier();
+                rescale(4 * t + 2);
+                lds_barrier();
+                mma_group(h, 3);
+                store_scales(h ^ 1, h ^ 1, 3, 4);
+                lds_barrier();
+            }
+        };
+        for (int t0 = 0; t0 < stages; t0 += 2) {
+            stage32(std::integral_constant<int, 0>{}, t0);
+            if (t0 + 1 < stages) stage32(std::integral_constant<int, 1>{}, t0 + 1);
+        }
+    } else
     for (int t0 = 0; t0 < stages; t0 += 2)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -544,6 +701,41 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
                 load_stage(t + 2, 0);
                 mma_stage(h, true, true);
                 lds_barrier();
+            }
+        } else if constexpr (GN) {
+            // Groups of 64, ping-pong per group: four phases per stage, the
+            // two groups' matrix work and rescales alternating as for groups
+            // of one stage.  The copy of stage t+1 is stored in this stage's
+            // matrix phases (its buffer was last read in the phase before
+            // this stage's first): two chunks and the scale rows in the
+            // first, one chunk in the second.  (Groups of 32 run the loop
+            // below.)
+            if constexpr (NG == 2) {
+                if (EARLY) {
+                    load_stage(t + 2, h);
+                    mma_group(h, 0);
+                    store_stage(h ^ 1, h ^ 1, 0, 2, true);
+                    lds_barrier();
+                    rescale(2 * t);
+                    lds_barrier();
+                    mma_group(h, 1);
+                    store_stage(h ^ 1, h ^ 1, 2, NCH, false);
+                    lds_barrier();
+                    rescale(2 * t + 1);
+                    lds_barrier();
+                } else {
+                    if (t > 0) rescale(2 * t - 1);
+                    lds_barrier();
+                    load_stage(t + 2, h);
+                    mma_group(h, 0);
+                    store_stage(h ^ 1, h ^ 1, 0, 2, true);
+                    lds_barrier();
+                    rescale(2 * t);
+                    lds_barrier();
+                    mma_group(h, 1);
+                    store_stage(h ^ 1, h ^ 1, 2, NCH, false);
+                    lds_barrier();
+                }
             }
         } else {
         if (SPG == 0) {
@@ -607,6 +799,8 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
     } else if (!EARLY && SPG == 1) {
         // the last stage ends the last group
         rescale(stages - 1);
+    } else if (!EARLY && GN) {
+        rescale(NG * stages - 1);
     }
 
     if (a.part) {
@@ -650,7 +844,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared& sh)
 template <bool MIXED, bool DEBUG_P, int SPG, bool F8 = false>
 __global__ __launch_bounds__(THREADS, 2) void gemm_pp_kernel(PPArgs a)
 {
-    __shared__ PPShared sh;
+    __shared__ PPShared<PPMode<SPG>::NG, PPMode<SPG>::HV> sh;
     // wave-uniform role (a scalar branch)
     if (__builtin_amdgcn_readfirstlane(threadIdx.x) < THREADS / 2)
         pp_body<MIXED, DEBUG_P, SPG, true, F8>(a, sh);
@@ -754,7 +948,7 @@ PingpongSplit pingpong_split(const GemmProblem& p)
     // rounds of `cus` tiles.  When the last round (the only one, for few
     // tiles) is at most half full, its tiles are split over K into
     // nparts = min(cus / tiles, stages / 2, 4) parts (at group boundaries:
-    // groups of one stage only), which fills up to nparts times as many CUs
+    // groups of one stage or half a stage only), which fills up to nparts times as many CUs
     // for 1/nparts of the time; the reduction reads nparts partial tiles
     // (more parts measured slower: their fp32 partial tiles cost more traffic
     // than the shorter K saves).
@@ -763,7 +957,7 @@ PingpongSplit pingpong_split(const GemmProblem& p)
     const int gs = p.ga < p.gw ? p.ga : p.gw;
     const int cus = cu_count();
     const int stages = p.K / KSTAGE;
-    if (gs != KSTAGE || stages < 4 || cus <= 0) return sp;
+    if ((gs != KSTAGE && gs != KSTAGE / 2 && gs != KSTAGE / 4) || stages < 4 || cus <= 0) return sp;
     const int tail = sp.tiles % cus;
     if (tail == 0 || 2 * tail > cus) return sp;
     int parts = cus / tail;
@@ -779,11 +973,15 @@ bool pingpong_supports(const GemmProblem& p)
 {
     const int gs = p.ga < p.gw ? p.ga : p.gw;
     const bool mixed = p.gw == p.K && p.ga != p.gw;
-    // groups of one stage (128), two stages (256) or one group (K); mixed
-    // mode with activation groups of one or two stages
-    if (!(gs == KSTAGE || gs == 2 * KSTAGE || (gs == p.K && gs % KSTAGE == 0))) return false;
+    // groups of a quarter stage (32), half a stage (64), one stage (128), two
+    // stages (256) or one group (K); mixed mode with activation groups of
+    // half a stage, one or two stages
+    if (!(gs == KSTAGE / 4 || gs == KSTAGE / 2 || gs == KSTAGE || gs == 2 * KSTAGE ||
+          (gs == p.K && gs % KSTAGE == 0)))
+        return false;
+    if (p.K % KSTAGE != 0) return false;
     if (!mixed && p.ga != p.gw) return false;
-    if (mixed && p.ga != KSTAGE && p.ga != 2 * KSTAGE) return false;
+    if (mixed && p.ga != KSTAGE / 2 && p.ga != KSTAGE && p.ga != 2 * KSTAGE) return false;
     // 32-bit buffer offsets within one workgroup's rows
     const uint64_t rowbytes = (uint64_t)p.K / 2;
     return rowbytes * BM < (1ull << 31) && (uint64_t)p.K / gs * 4 * BM < (1ull << 31);
@@ -832,7 +1030,7 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     t.Ga = p.K / p.ga;
     t.Gw = p.K / p.gw;
     const int gs = p.ga < p.gw ? p.ga : p.gw;
-    t.spg = gs / KSTAGE;
+    t.spg = gs == KSTAGE / 2 ? -1 : gs == KSTAGE / 4 ? -2 : gs / KSTAGE;
     t.G = p.K / gs;
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
@@ -851,9 +1049,13 @@ hipError_t launch_gemm_pingpong(const GemmProblem& p, hipStream_t stream)
     if (sp.tail && (!p.ws || p.ws_bytes < sp.bytes)) sp.tail = 0;
     sp.part = static_cast<float*>(p.ws);
     const bool mixed = p.gw == p.K && p.ga != p.gw;
-    // mixed mode here: ga = 128 or 256 (the activation groups are 1 or 2 stages)
-    if (mixed && t.spg == 1) launch_pp_all<true, 1>(t, sp, stream);
+    // mixed mode here: ga = 64, 128 or 256 (the activation groups are half a
+    // stage, 1 or 2 stages)
+    if (mixed && gs == KSTAGE / 2) launch_pp_all<true, -1>(t, sp, stream);
+    else if (mixed && t.spg == 1) launch_pp_all<true, 1>(t, sp, stream);
     else if (mixed) launch_pp_all<true, 2>(t, sp, stream);
+    else if (gs == KSTAGE / 2) launch_pp_all<false, -1>(t, sp, stream);
+    else if (gs == KSTAGE / 4) launch_pp_all<false, -2>(t, sp, stream);
     else if (t.spg == 1) launch_pp_all<false, 1>(t, sp, stream);
     else if (gs == p.K) launch_pp_all<false, 0>(t, sp, stream);
     else launch_pp_all<false, 2>(t, sp, stream);

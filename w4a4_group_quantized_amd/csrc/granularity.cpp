@@ -9,7 +9,7 @@
 // work in whole 256-row tiles, the weight-streaming kernels of decode shapes
 // (up to 64 rows, groups of at least 128) are bound by the bytes they read.
 // Groups of 32 and 64 have no streaming kernel, so at decode sizes they run
-// a tiled kernel on mostly empty tiles, ten times slower or more.
+// a tiled kernel on mostly empty tiles, five times slower or more.
 // Host code only.
 #include "apex4.h"
 
@@ -36,12 +36,12 @@ struct Mode {
 // finest first: activation groups first (the activations carry the outliers),
 // then weight groups
 constexpr Mode kModes[] = {
-    {32, 32, {451, 494, 563, 580}, {0, 0, 0, 0}},
-    {64, 64, {665, 764, 830, 829}, {0, 0, 0, 0}},
-    {128, 128, {1417, 1411, 1606, 1646}, {5.28, 4.33, 4.27, 2.03}},
-    {128, 0, {1437, 1438, 1720, 1737}, {5.24, 4.29, 4.14, 1.99}},   // mixed: per-channel weights
-    {256, 256, {1558, 1650, 1809, 1796}, {5.27, 4.33, 4.22, 1.86}},
-    {0, 0, {1923, 1997, 2342, 2344}, {5.20, 4.42, 4.49, 2.30}},     // per-channel on both operands
+    {32, 32, {497, 546, 603, 602}, {0, 0, 0, 0}},
+    {64, 64, {1040, 1072, 1218, 1249}, {0, 0, 0, 0}},
+    {128, 128, {1355, 1394, 1617, 1627}, {5.28, 4.33, 4.27, 2.03}},
+    {128, 0, {1417, 1410, 1712, 1729}, {5.24, 4.29, 4.14, 1.99}},   // mixed: per-channel weights
+    {256, 256, {1516, 1623, 1799, 1791}, {5.27, 4.33, 4.22, 1.86}},
+    {0, 0, {1886, 1991, 2339, 2361}, {5.20, 4.42, 4.49, 2.30}},     // per-channel on both operands
 };
 
 constexpr double kHbmBytesPerS = 5.0e12;   // what the tiled kernels' operand reads can reach
