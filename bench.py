@@ -311,11 +311,19 @@ def write_traffic(prof_dir, workloads):
     cal = {"copy_fetch_kib_per_GiB": copies("FETCH_SIZE"), "copy_write_kib_per_GiB": copies("WRITE_SIZE")}
     cal["fetch_factor"] = gib_kib / cal["copy_fetch_kib_per_GiB"]
     cal["write_factor"] = gib_kib / cal["copy_write_kib_per_GiB"]
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    # records of workloads not counted in this set are kept (each with its own calibration)
+    try:
+        with open(path) as f:
+            kept = json.load(f).get("workloads", {})
+    except (OSError, ValueError):
+        kept = {}
     out = {"description": "HBM bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                           "(KiB per dispatch), each scaled by the factor that makes the same counter read "
-                          "1 GiB for a plain 1 GiB device copy; written by python bench.py --write-traffic. "
+                          "1 GiB for a plain 1 GiB device copy (the calibration of the run that counted "
+                          "the workload); written by python bench.py --write-traffic. "
                           "bench.py reports them only while the sources of the workload's kernels hash the same.",
-           "calibration": cal, "workloads": {}}
+           "workloads": {w: r for w, r in kept.items() if w not in workloads}}
     for wl in workloads:
         # (FP8-coded operands: one byte per code, (M + N) K / 2 more bytes read;
         # FP6: (M + N) K / 4 more)
@@ -336,13 +344,13 @@ def write_traffic(prof_dir, workloads):
                         "algorithmic_bytes": rl.gemm_bytes(M, N, K, ga, gw) + ((M + N) * K / 2 if f8 else 0)
                         + ((M + N) * K / 4 if f6 else 0)})
         out["workloads"][wl] = {
+            "calibration": cal,
             "kernel_sources": files,
             "kernel_sources_sha256": kernel_sources_sha256(files),
             "hbm_bytes_per_launch": float(np.mean([p["fetch_bytes"] + p["write_bytes"] for p in per])),
             "algorithmic_bytes_per_launch": float(np.mean([p["algorithmic_bytes"] for p in per])),
             "per_layer": per,
         }
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({w: out["workloads"][w]["hbm_bytes_per_launch"] for w in workloads}))
