@@ -66,7 +66,8 @@ WORKLOADS = {
 }
 # The same layer sets on FP8-coded operands (apex4_quantize_f8, apex4_gemm_w4a4_f8):
 # name -> the INT4 workload it mirrors
-F8_WORKLOADS = {"llama2-7b-prefill-f8": "llama2-7b-prefill", "llama2-70b-prefill-f8": "llama2-70b-prefill"}
+F8_WORKLOADS = {"llama2-7b-prefill-f8": "llama2-7b-prefill", "llama2-70b-prefill-f8": "llama2-70b-prefill",
+                "sweep-g64-f8": "sweep-g64"}
 # ... and on FP6-coded operands (apex4_quantize_f6, apex4_gemm_w4a4_f6: each code a 6-bit E2M3 field)
 F6_WORKLOADS = {"llama2-7b-prefill-f6": "llama2-7b-prefill", "llama2-70b-prefill-f6": "llama2-70b-prefill",
                 "sweep-g128-f6": "sweep-g128"}
@@ -119,7 +120,7 @@ def parse():
                          "(M:K:N,M:K:N,...; back-to-back launches, weights cycled past the "
                          "last-level cache) and print one JSON line of rates per shape: the "
                          "measurements behind apex4_select_granularity")
-    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8,llama2-70b-prefill-f6,sweep-g32,sweep-g64",
+    ap.add_argument("--traffic-workloads", default="llama2-7b-prefill,llama2-70b-prefill,llama2-70b-decode-m1,llama2-70b-decode-m4,llama2-70b-decode-m16,llama2-70b-decode-m64,llama2-7b-prefill-f8,llama2-70b-prefill-f6,sweep-g32,sweep-g64,sweep-g64-f8",
                     help="workloads for --write-traffic (comma-separated)")
     return ap.parse_args()
 

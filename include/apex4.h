@@ -217,27 +217,31 @@ apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* q
  * ahead; the APEX4 page's own kernels run on INT4 tensor cores.)
  *
  * apex4_quantize_f8: the quantization rule of apex4_quantize_act /
- * apex4_pack_weight (groups of 128), codes written as E4M3 bytes, one per
- * element in K order (-0 is written as +0).
- *   x_f16 [rows, K] fp16, 16-byte aligned; rows >= 0 (0: no-op), K % 128 == 0.
- *   q8 [rows, K] bytes, 8-byte aligned;  s [rows, K/128] fp32, as apex4_quantize_act.
- *   group: 128 only (other valid groups: APEX4_ERR_UNSUPPORTED).
+ * apex4_pack_weight (groups of 64 or 128), codes written as E4M3 bytes, one
+ * per element in K order (-0 is written as +0).
+ *   x_f16 [rows, K] fp16, 16-byte aligned; rows >= 0 (0: no-op), K % group == 0.
+ *   q8 [rows, K] bytes, 8-byte aligned;  s [rows, K/group] fp32, as apex4_quantize_act.
+ *   group: 64 or 128 (other valid groups: APEX4_ERR_UNSUPPORTED).
  */
 apex4_status apex4_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q8,
                                float* s, void* stream);
 
 /*
- * apex4_gemm_w4a4_f8: Y of apex4_gemm_w4a4 with group_a = group_w = 128 from
- * E4M3-coded operands (apex4_quantize_f8 outputs).
- *   qa8 [M, K], qw8 [N, K] bytes, 16-byte aligned; s_a [M, K/128], s_w [N, K/128].
- *   y_f16 [M, N], y_f32 [M, N] or NULL, psum_dbg [M, N, K/128] int32 or NULL,
+ * apex4_gemm_w4a4_f8: Y of apex4_gemm_w4a4 with group_a = group_w = group
+ * from E4M3-coded operands (apex4_quantize_f8 outputs).
+ *   qa8 [M, K], qw8 [N, K] bytes, 16-byte aligned; s_a [M, K/group], s_w [N, K/group].
+ *   group: 64 or 128 on both operands (other divisors of K: APEX4_ERR_UNSUPPORTED).
+ *   At groups of 64 the matrix instruction's fp32 result is the group sum
+ *   itself, and the rescale is one fma per output and group where the INT4
+ *   path also converts the int32 sum.
+ *   y_f16 [M, N], y_f32 [M, N] or NULL, psum_dbg [M, N, K/group] int32 or NULL,
  *   as in apex4_gemm_w4a4 (the fp32 summation order is not fixed; P exact).
  *   M, N >= 0 (0: no-op), K > 0, K % 128 == 0, 256 * K < 2^31.  Any M works;
  *   the kernel is the compute-bound one (256 x 128 output tiles), meant for
  *   prefill-sized M.  No workspace.  Asynchronous on `stream`.
  */
 apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* qw8, const float* s_w,
-                                int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                int32_t group, int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
                                 int32_t* psum_dbg, void* stream);
 
 /*

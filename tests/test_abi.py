@@ -282,3 +282,20 @@ def test_noalloc_host_checks(L):
     text = open(os.path.join(ROOT, "include", "apex4.h")).read()
     m = re.search(r"#define APEX4_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == apex4.NOALLOC_MAX_WORKSPACE
+
+
+def test_f8_group_checks(L):
+    """apex4_quantize_f8 / apex4_gemm_w4a4_f8: groups of 64 and 128 only, checked on the
+    host before any pointer is used (M = 0 would otherwise be a no-op)."""
+    assert L.apex4_quantize_f8(A16, 4, 1024, 32, A16b, A16b, None) == UNSUPPORTED
+    assert L.apex4_quantize_f8(A16, 4, 1024, 256, A16b, A16b, None) == UNSUPPORTED
+    assert L.apex4_quantize_f8(A16, 4, 1024, 96, A16b, A16b, None) == INVALID     # does not divide K
+    f = L.apex4_gemm_w4a4_f8
+    assert f(A16, A16b, A16, A16b, 32, 0, 8, 1024, A16, None, None, None) == UNSUPPORTED
+    assert f(A16, A16b, A16, A16b, 256, 0, 8, 1024, A16, None, None, None) == UNSUPPORTED
+    assert f(A16, A16b, A16, A16b, 96, 0, 8, 1024, A16, None, None, None) == INVALID
+    assert f(A16, A16b, A16, A16b, 0, 0, 8, 1024, A16, None, None, None) == INVALID
+    assert f(A16, A16b, A16, A16b, 64, 8, 8, 1000, A16, None, None, None) == INVALID   # K % 128
+    for g in (64, 128):
+        assert f(A16, A16b, A16, A16b, g, 0, 8, 1024, A16, None, None, None) == OK    # no-op
+        assert f(MIS, A16b, A16, A16b, g, 8, 8, 1024, A16, None, None, None) == ALIGN

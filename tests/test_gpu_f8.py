@@ -56,13 +56,14 @@ def test_e4m3_decoder_pins():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("g", [64, 128])
 @pytest.mark.parametrize("kind", inputs.ACT_KINDS)
 @pytest.mark.parametrize("rows,K", [(1, 128), (37, 1152), (300, 4096)])
-def test_quantize_f8_codes(dev, kind, rows, K):
+def test_quantize_f8_codes(dev, kind, rows, K, g):
     x, _ = inputs.problem(rows, 8, K, seed=rows + K, act=kind)
-    q8, s = apex4.quantize_f8(torch.from_numpy(x).to(dev), 128)
+    q8, s = apex4.quantize_f8(torch.from_numpy(x).to(dev), g)
     torch.cuda.synchronize()
-    oq, os_ = orc.quantize(x, 128)
+    oq, os_ = orc.quantize(x, g)
     codes = unpack_codes(oq)
     got = e4m3_value(q8.cpu().numpy())
     assert np.array_equal(got, codes.astype(np.float64))
@@ -70,17 +71,17 @@ def test_quantize_f8_codes(dev, kind, rows, K):
     assert not np.any(q8.cpu().numpy() == 0x80)          # no -0
 
 
-def run_f8(dev, x, w, rows=None, want_p=True):
+def run_f8(dev, x, w, rows=None, want_p=True, g=128):
     tx, tw = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
-    qa8, sa = apex4.quantize_f8(tx, 128)
-    qw8, sw = apex4.quantize_f8(tw, 128)
-    y16, y32, ps = apex4.gemm_f8(qa8, sa, qw8, sw, want_y32=True, want_psum=want_p)
+    qa8, sa = apex4.quantize_f8(tx, g)
+    qw8, sw = apex4.quantize_f8(tw, g)
+    y16, y32, ps = apex4.gemm_f8(qa8, sa, qw8, sw, g, want_y32=True, want_psum=want_p)
     torch.cuda.synchronize()
     K = x.shape[1]
-    oqa, osa = orc.quantize(x, 128)
-    oqw, osw = orc.quantize(w, 128)
+    oqa, osa = orc.quantize(x, g)
+    oqw, osw = orc.quantize(w, g)
     r = np.arange(x.shape[0]) if rows is None else rows
-    _, o32, op = orc.gemm(oqa[r], osa[r], 128, oqw, osw, 128, K, want_p=want_p)
+    _, o32, op = orc.gemm(oqa[r], osa[r], g, oqw, osw, g, K, want_p=want_p)
     y32n, y16n = y32.cpu().numpy()[r], y16.cpu().numpy()[r]
     scale = float(np.abs(o32).max())
     tol = REL_TOL * max(scale, 1e-30)
@@ -95,27 +96,29 @@ def run_f8(dev, x, w, rows=None, want_p=True):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("g", [64, 128])
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 1024), (300, 300, 384), (257, 130, 1152), (513, 257, 2048)])
-def test_gemm_f8_matches_oracle(dev, M, N, K):
-    """Ragged M and N, odd group counts (3 and 9 groups: a group is two
-    64-code stages)."""
+def test_gemm_f8_matches_oracle(dev, M, N, K, g):
+    """Ragged M and N, odd stage counts (3 and 9 stages of 128 codes: one
+    group of 128 or two of 64 each)."""
     x, w = inputs.problem(M, N, K, seed=71 + M, act="outlier")
-    run_f8(dev, x, w)
+    run_f8(dev, x, w, g=g)
 
 
 @pytest.mark.gpu
-def test_gemm_f8_equals_int4_path(dev):
+@pytest.mark.parametrize("g", [64, 128])
+def test_gemm_f8_equals_int4_path(dev, g):
     # a whole number of rounds of 256x128 tiles (512 x 64 CUs columns), so the
     # INT4 path runs over all of K in every tile, with no K split, and both
     # add the groups in the same order
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     x, w = inputs.problem(512, 64 * cus, 2048, seed=5, act="student_t")
     rows = np.array([0, 1, 255, 256, 300, 511])
-    tx, tw, y32 = run_f8(dev, x, w, rows=rows)
-    qa, sa = apex4.quantize_act(tx, 128)
-    qw, sw = apex4.pack_weight(tw, 128)
-    assert apex4.workspace_size(512, 64 * cus, 2048, 128, 128) == 0
-    _, y32i, _ = apex4.gemm(qa, sa, 128, qw, sw, 128, 2048, want_y32=True)
+    tx, tw, y32 = run_f8(dev, x, w, rows=rows, g=g)
+    qa, sa = apex4.quantize_act(tx, g)
+    qw, sw = apex4.pack_weight(tw, g)
+    assert apex4.workspace_size(512, 64 * cus, 2048, g, g) == 0
+    _, y32i, _ = apex4.gemm(qa, sa, g, qw, sw, g, 2048, want_y32=True)
     torch.cuda.synchronize()
     assert torch.equal(y32.view(torch.int32), y32i.view(torch.int32))
 
@@ -131,8 +134,12 @@ def test_gemm_f8_full_7b_qkv(dev):
 def test_f8_argument_checks(dev):
     x = torch.zeros((4, 256), dtype=torch.float16, device=dev)
     with pytest.raises(apex4.Apex4Error):
-        apex4.quantize_f8(x, 64)
+        apex4.quantize_f8(x, 32)                          # groups of 64 and 128 only
     q8 = torch.zeros((4, 200), dtype=torch.uint8, device=dev)
     s = torch.ones((4, 1), dtype=torch.float32, device=dev)
     with pytest.raises(apex4.Apex4Error):
         apex4.gemm_f8(q8, s, q8, s)                      # K = 200 is not a multiple of 128
+    q8 = torch.zeros((4, 256), dtype=torch.uint8, device=dev)
+    s = torch.ones((4, 8), dtype=torch.float32, device=dev)
+    with pytest.raises(apex4.Apex4Error):
+        apex4.gemm_f8(q8, s, q8, s)                      # groups of 32: no FP8 kernel

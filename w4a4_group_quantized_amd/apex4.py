@@ -38,7 +38,7 @@ SIGNATURES = {
     "apex4_linear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "apex4_linear_w4a4": (_I32, [_P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_quantize_f8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
-    "apex4_gemm_w4a4_f8": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "apex4_gemm_w4a4_f8": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P]),
     "apex4_quantize_f6": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "apex4_gemm_w4a4_f6": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "apex4_select_granularity": (_I32, [_I64, _I64, _I64, ctypes.c_double,
@@ -247,7 +247,8 @@ def linear(x, ga: int, qw, sw, gw: int, *, want_y32: bool = False, y16=None, y32
 
 def quantize_f8(x, group: int = 128, out=None):
     """x: fp16 [rows, K] GPU tensor -> (q8 uint8 [rows, K] E4M3 codes, s float32 [rows, K/group])
-    (apex4_quantize_f8: the rule of quantize_act / pack_weight, one byte per code)."""
+    (apex4_quantize_f8: the rule of quantize_act / pack_weight, one byte per code; groups of 64
+    or 128)."""
     import torch
     _need_gpu(x, "x", torch.float16)
     rows, K = x.shape
@@ -263,17 +264,21 @@ def quantize_f8(x, group: int = 128, out=None):
     return q8, s
 
 
-def gemm_f8(qa8, sa, qw8, sw, *, want_y32: bool = False, want_psum: bool = False, y16=None, y32=None):
-    """apex4_gemm_w4a4_f8: the W4A4 GEMM (groups of 128) on E4M3-coded operands.
-    Returns y16, or (y16, y32, psum) when want_y32/want_psum is set."""
+def gemm_f8(qa8, sa, qw8, sw, group: int | None = None, *, want_y32: bool = False, want_psum: bool = False,
+            y16=None, y32=None):
+    """apex4_gemm_w4a4_f8: the W4A4 GEMM (groups of 64 or 128 on both operands; None: K / the
+    scale columns) on E4M3-coded operands.  Returns y16, or (y16, y32, psum) when
+    want_y32/want_psum is set."""
     import torch
     M, K = qa8.shape
     N = qw8.shape[0]
     dev = qa8.device
+    if group is None:
+        group = K // sa.shape[1] if sa.dim() == 2 and sa.shape[1] > 0 else 0
     _need_gpu(qa8, "qa8", torch.uint8, (M, K), dev)
     _need_gpu(qw8, "qw8", torch.uint8, (N, K), dev)
-    _need_gpu(sa, "s_a", torch.float32, (M, K // 128), dev)
-    _need_gpu(sw, "s_w", torch.float32, (N, K // 128), dev)
+    _need_gpu(sa, "s_a", torch.float32, (M, _cols(K, group)), dev)
+    _need_gpu(sw, "s_w", torch.float32, (N, _cols(K, group)), dev)
     # caller buffers are checked before anything is allocated
     if y16 is not None:
         _need_gpu(y16, "y16", torch.float16, (M, N), dev)
@@ -283,9 +288,9 @@ def gemm_f8(qa8, sa, qw8, sw, *, want_y32: bool = False, want_psum: bool = False
         y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
     if want_y32 and y32 is None:
         y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
-    psum = torch.empty((M, N, K // 128), dtype=torch.int32, device=dev) if want_psum else None
+    psum = torch.empty((M, N, _cols(K, group)), dtype=torch.int32, device=dev) if want_psum else None
     _check("apex4_gemm_w4a4_f8", lib().apex4_gemm_w4a4_f8(
-        _ptr(qa8), _ptr(sa), _ptr(qw8), _ptr(sw), M, N, K, _ptr(y16), _ptr(y32), _ptr(psum),
+        _ptr(qa8), _ptr(sa), _ptr(qw8), _ptr(sw), group, M, N, K, _ptr(y16), _ptr(y32), _ptr(psum),
         _stream(torch, dev)))
     if want_y32 or want_psum:
         return y16, y32, psum

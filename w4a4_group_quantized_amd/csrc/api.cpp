@@ -148,20 +148,23 @@ apex4_status apex4_linear_w4a4(const void* x_f16, int32_t group_a, const void* q
 apex4_status apex4_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int32_t group, void* q8,
                                float* s, void* stream)
 {
-    if (group != 128) return group > 0 && K > 0 && K % group == 0 ? APEX4_ERR_UNSUPPORTED : APEX4_ERR_INVALID_ARG;
+    if (group != 128 && group != 64)
+        return group > 0 && K > 0 && K % group == 0 ? APEX4_ERR_UNSUPPORTED : APEX4_ERR_INVALID_ARG;
     const apex4_status st = check_quantize(x_f16, rows, K, group, q8, s);
     if (st != APEX4_OK || rows == 0) return st;
     if (!aligned(q8, 8)) return APEX4_ERR_ALIGNMENT;
-    return to_status(apex4::launch_quantize_f8(x_f16, rows, K, q8, s, static_cast<hipStream_t>(stream)));
+    return to_status(apex4::launch_quantize_f8(x_f16, rows, K, group, q8, s, static_cast<hipStream_t>(stream)));
 }
 
 apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* qw8, const float* s_w,
-                                int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32, int32_t* psum_dbg,
-                                void* stream)
+                                int32_t group, int64_t M, int64_t N, int64_t K, void* y_f16, float* y_f32,
+                                int32_t* psum_dbg, void* stream)
 {
     if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim || K <= 0 || K > kMaxDim || K % 128 != 0)
         return APEX4_ERR_INVALID_ARG;
-    if (psum_dbg && (unsigned __int128)M * (uint64_t)N * (uint64_t)(K / 128) > (uint64_t)kMaxDim)
+    if (group <= 0 || K % group != 0) return APEX4_ERR_INVALID_ARG;
+    if (group != 128 && group != 64) return APEX4_ERR_UNSUPPORTED;
+    if (psum_dbg && (unsigned __int128)M * (uint64_t)N * (uint64_t)(K / group) > (uint64_t)kMaxDim)
         return APEX4_ERR_INVALID_ARG;
     // 32-bit offsets within a 256-row block of operand bytes
     if ((uint64_t)K * 256 >= (1ull << 31)) return APEX4_ERR_UNSUPPORTED;
@@ -178,8 +181,8 @@ apex4_status apex4_gemm_w4a4_f8(const void* qa8, const float* s_a, const void* q
     p.M = static_cast<int32_t>(M);
     p.N = static_cast<int32_t>(N);
     p.K = static_cast<int32_t>(K);
-    p.ga = 128;
-    p.gw = 128;
+    p.ga = group;
+    p.gw = group;
     p.y16 = y_f16;
     p.y32 = y_f32;
     p.psum = psum_dbg;

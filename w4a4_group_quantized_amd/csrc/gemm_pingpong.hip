@@ -514,6 +514,28 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
         constexpr int KS = 4 / NG;   // 32-value K-steps per group
         const uint8_t* la = sh.a[buf] + frag + 32 * KS * q;
         const uint8_t* lb = sh.b[buf] + fragb + 32 * KS * q;
+        if constexpr (F8) {
+            // FP8 operands, groups of 64: one 64-value K-step of the FP8 MFMA
+            // per tile (32 bytes per lane), whose fp32 result is the group sum
+            v8i ga[2], gb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v4i a0 = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE);
+                const v4i a1 = *reinterpret_cast<const v4i*>(la + i * 32 * STRIDE + 16);
+                const v4i b0 = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE);
+                const v4i b1 = *reinterpret_cast<const v4i*>(lb + i * 32 * STRIDE + 16);
+                ga[i] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                gb[i] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    P[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga[mt], gb[nt], v16f{}, 0, 0, 0, 127,
+                                                                                0, 127);
+            scale_products(buf, q);
+            return;
+        }
         v4i fa[2][KS], fb[2][KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
@@ -686,8 +708,34 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
         if constexpr (F8) {
             // FP8 operands, groups of one stage: the ping-pong as below with
             // the copy's single register set stored (stage t+1) before the
-            // loads of stage t+2 are issued into it
-            if (EARLY) {
+            // loads of stage t+2 are issued into it.  Groups of 64: the same
+            // per group, four phases per stage (the copy in the first matrix
+            // phase).
+            if constexpr (GN) {
+                if (EARLY) {
+                    store_stage(h ^ 1, 0);
+                    load_stage(t + 2, 0);
+                    mma_group(h, 0);
+                    lds_barrier();
+                    rescale(2 * t);
+                    lds_barrier();
+                    mma_group(h, 1);
+                    lds_barrier();
+                    rescale(2 * t + 1);
+                    lds_barrier();
+                } else {
+                    if (t > 0) rescale(2 * t - 1);
+                    lds_barrier();
+                    store_stage(h ^ 1, 0);
+                    load_stage(t + 2, 0);
+                    mma_group(h, 0);
+                    lds_barrier();
+                    rescale(2 * t);
+                    lds_barrier();
+                    mma_group(h, 1);
+                    lds_barrier();
+                }
+            } else if (EARLY) {
                 store_stage(h ^ 1, 0);
                 load_stage(t + 2, 0);
                 mma_stage(h, true, true);
@@ -989,8 +1037,8 @@ bool pingpong_supports(const GemmProblem& p)
 
 hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
 {
-    // FP8-coded operands (qa, qw: [rows, K] bytes), groups of 128 on both
-    // operands (one stage per group)
+    // FP8-coded operands (qa, qw: [rows, K] bytes), groups of 128 (one stage
+    // per group) or 64 (two per stage) on both operands
     PPArgs t{};
     t.qa = p.qa;
     t.sa = p.sa;
@@ -999,10 +1047,11 @@ hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
     t.M = p.M;
     t.N = p.N;
     t.K = p.K;
-    t.Ga = p.K / 128;
-    t.Gw = p.K / 128;
-    t.spg = 1;
-    t.G = p.K / 128;
+    const int g = p.ga;   // 64 or 128, both operands
+    t.Ga = p.K / g;
+    t.Gw = p.K / g;
+    t.spg = g == KSTAGE / 2 ? -1 : 1;
+    t.G = p.K / g;
     t.y16 = static_cast<_Float16*>(p.y16);
     t.y32 = p.y32;
     t.psum = p.psum;
@@ -1012,8 +1061,13 @@ hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream)
     t.group_m = tile_band_rows(t.tiles_m);
     t.nparts = 1;
     const int tiles = ((p.M + BM - 1) / BM) * t.tiles_n;
-    if (t.psum) gemm_pp_kernel<false, true, 1, true><<<tiles, THREADS, 0, stream>>>(t);
-    else gemm_pp_kernel<false, false, 1, true><<<tiles, THREADS, 0, stream>>>(t);
+    if (g == KSTAGE / 2) {
+        if (t.psum) gemm_pp_kernel<false, true, -1, true><<<tiles, THREADS, 0, stream>>>(t);
+        else gemm_pp_kernel<false, false, -1, true><<<tiles, THREADS, 0, stream>>>(t);
+    } else {
+        if (t.psum) gemm_pp_kernel<false, true, 1, true><<<tiles, THREADS, 0, stream>>>(t);
+        else gemm_pp_kernel<false, false, 1, true><<<tiles, THREADS, 0, stream>>>(t);
+    }
     return hipGetLastError();
 }
 

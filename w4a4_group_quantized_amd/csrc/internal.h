@@ -97,7 +97,7 @@ hipError_t launch_gemm_pingpong_f8(const GemmProblem& p, hipStream_t stream);
 bool f6_supports(const GemmProblem& p);
 hipError_t launch_gemm_f6(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_quantize_f6(const void* x_f16, int64_t rows, int64_t K, void* q6, float* s, hipStream_t stream);
-hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* q8, float* s,
+hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int group, void* q8, float* s,
                               hipStream_t stream);
 bool gemv_supports(const GemmProblem& p);
 hipError_t launch_gemm_gemv(const GemmProblem& p, hipStream_t stream);

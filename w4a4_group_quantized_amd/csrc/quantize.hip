@@ -165,12 +165,15 @@ hipError_t launch_quantize(const void* x_f16, int64_t rows, int64_t K, int32_t g
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, void* q8, float* s,
+hipError_t launch_quantize_f8(const void* x_f16, int64_t rows, int64_t K, int group, void* q8, float* s,
                               hipStream_t stream)
 {
+    // group: 64 or 128, checked by the caller
     const int64_t n8 = rows * (K / 8);
     const unsigned blocks = (unsigned)((n8 + 255) / 256);
-    quantize_groups_kernel<128, true><<<blocks, 256, 0, stream>>>(static_cast<const half8*>(x_f16), n8, q8, s);
+    const half8* x = static_cast<const half8*>(x_f16);
+    if (group == 64) quantize_groups_kernel<64, true><<<blocks, 256, 0, stream>>>(x, n8, q8, s);
+    else quantize_groups_kernel<128, true><<<blocks, 256, 0, stream>>>(x, n8, q8, s);
     return hipGetLastError();
 }
 
