@@ -626,13 +626,18 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
     // Stage t uses A/B and scale buffer t&1 and register set t&1; the loop is
     // unrolled by two so that these are compile-time indices.
     if constexpr (NG == 4) {
-        // Groups of 32, ping-pong per group: eight phases per stage, the four
-        // groups' matrix work and rescales alternating as for groups of one
-        // stage.  The copy of stage t+1 is stored in the first three matrix
-        // phases, one chunk each, and group q's scale rows in matrix phase q
-        // (its buffer was last read in the phase before this stage's first).  The
-        // buffer parity h is a template constant here (the stage body is too
-        // large for the compiler to unroll the loop below).
+        // Groups of 32: per wave, each group's matrix work followed by the
+        // rescale of the group before, the late waves one group behind the
+        // early ones, with one barrier per stage: the copy of stage t+1 goes
+        // to the buffer that every wave finished reading before the last
+        // barrier, and is read only after the next one, so the barriers
+        // between the groups' phases were only keeping the two waves of a
+        // SIMD in opposite roles (with them, eight per stage, 602 TOPS on the
+        // sweep shape; without, 684 on the same box).  The copy of stage t+1
+        // is stored with the first three groups' matrix work, one chunk each,
+        // and group q's scale rows with group q's.  The buffer parity h is a
+        // template constant here (the stage body is too large for the
+        // compiler to unroll the loop below).
         auto stage32 = [&](auto hc, int t) __attribute__((always_inline)) {
             constexpr int h = decltype(hc)::value;
             if (EARLY) {
@@ -640,48 +645,34 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
                 mma_group(h, 0);
                 store_stage(h ^ 1, h ^ 1, 0, 1, false);
                 store_scales(h ^ 1, h ^ 1, 0, 1);
-                lds_barrier();
                 rescale(4 * t);
-                lds_barrier();
                 mma_group(h, 1);
                 store_stage(h ^ 1, h ^ 1, 1, 2, false);
                 store_scales(h ^ 1, h ^ 1, 1, 2);
-                lds_barrier();
                 rescale(4 * t + 1);
-                lds_barrier();
                 mma_group(h, 2);
                 store_stage(h ^ 1, h ^ 1, 2, NCH, false);
                 store_scales(h ^ 1, h ^ 1, 2, 3);
-                lds_barrier();
                 rescale(4 * t + 2);
-                lds_barrier();
                 mma_group(h, 3);
                 store_scales(h ^ 1, h ^ 1, 3, 4);
-                lds_barrier();
                 rescale(4 * t + 3);
                 lds_barrier();
             } else {
                 if (t > 0) rescale(4 * t - 1);
-                lds_barrier();
                 load_stage(t + 2, h);
                 mma_group(h, 0);
                 store_stage(h ^ 1, h ^ 1, 0, 1, false);
                 store_scales(h ^ 1, h ^ 1, 0, 1);
-                lds_barrier();
                 rescale(4 * t);
-                lds_barrier();
                 mma_group(h, 1);
                 store_stage(h ^ 1, h ^ 1, 1, 2, false);
                 store_scales(h ^ 1, h ^ 1, 1, 2);
-                lds_barrier();
                 rescale(4 * t + 1);
-                lds_barrier();
                 mma_group(h, 2);
                 store_stage(h ^ 1, h ^ 1, 2, NCH, false);
                 store_scales(h ^ 1, h ^ 1, 2, 3);
-                lds_barrier();
                 rescale(4 * t + 2);
-                lds_barrier();
                 mma_group(h, 3);
                 store_scales(h ^ 1, h ^ 1, 3, 4);
                 lds_barrier();
@@ -817,11 +808,16 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
             // t, most of the copy of stage t+1.  Phase 2: rescale of stage
             // t's group and the rest of the copy (the matrix phase is the
             // longer one: one of the thread's three chunks is stored here;
-            // not in mixed mode, whose rescale is the longer)
+            // not in mixed mode, whose rescale is the longer).  Outside mixed
+            // mode one barrier per stage: the copy goes to the buffer every
+            // wave finished reading before the last barrier and is read after
+            // the next, so the barrier between the phases only kept the two
+            // waves of a SIMD in opposite roles (1524 -> 1567 TOPS on the
+            // sweep shape and +2.6% on the 70B prefill layers, one box)
             load_stage(t + 2, h);
             mma_stage(h, true, true);
             store_stage(h ^ 1, h ^ 1, 0, SPLIT, true);
-            lds_barrier();
+            if (MIXED) lds_barrier();
             rescale(t);
             store_stage(h ^ 1, h ^ 1, SPLIT, NCH, false);
             lds_barrier();
@@ -831,7 +827,7 @@ __device__ __forceinline__ void pp_body(const PPArgs& a, PPShared<PPMode<SPG>::N
             // t-1); phase 2: matrix work of stage t, the rest of the copy
             if (t > 0) rescale(t - 1);
             store_stage(h ^ 1, h ^ 1, SPLIT, NCH, false);
-            lds_barrier();
+            if (MIXED) lds_barrier();
             load_stage(t + 2, h);
             mma_stage(h, true, true);
             store_stage(h ^ 1, h ^ 1, 0, SPLIT, true);
