@@ -309,8 +309,8 @@ apex4_status apex4_gemm_w4a4_f6(const void* qa6, const float* s_a, const void* q
  *   - otherwise the tiled kernels, which work in whole 256-row tiles:
  *     max(bytes / 5.0e12 B/s, 2*M'*N*K / rate) with M' = M rounded up to a
  *     multiple of 256 and the rate interpolated from the measured TOPS at
- *     M' = 256, 2048, 4096, 8192 (g = 32: 497..603, 64: 1040..1249, 128:
- *     1355..1627, mixed: 1410..1729, 256: 1516..1799, K: 1886..2361).
+ *     M' = 256, 2048, 4096, 8192 (g = 32: 538..684, 64: 1017..1208, 128:
+ *     1363..1625, mixed: 1357..1696, 256: 1485..1761, K: 1863..2358).
  * Groups of 32 and 64 have no weight-streaming kernel: at decode sizes they
  * run on mostly empty 256-row tiles and are modelled (and measured) five or
  * more times slower.  The finest mode whose modelled speed is at least

@@ -16,14 +16,14 @@ def built():
 
 
 def test_prefill_picks_g128_at_65_percent():
-    # compute-bound, M = 2048: 1394/1991 = 0.700 >= 0.65 > 1072/1991 = 0.538 (g=64)
+    # compute-bound, M = 2048: 1453/1975 = 0.736 >= 0.65 > 1049/1975 = 0.531 (g=64)
     assert apex4.select_granularity(2048, 12288, 4096, 0.65) == (128, 128)
 
 
 def test_prefill_picks_g64_at_half_speed():
-    # groups of 64 on the ping-pong kernel: 1072/1991 = 0.538 (M = 2048) and
-    # 1249/2361 = 0.529 (M = 8192) qualify at 0.5, g=32 (546/1991 = 0.274,
-    # 602/2361 = 0.255) does not
+    # groups of 64 on the ping-pong kernel: 1049/1975 = 0.531 (M = 2048) and
+    # 1208/2358 = 0.512 (M = 8192) qualify at 0.5, g=32 (580/1975 = 0.294,
+    # 684/2358 = 0.290) does not
     assert apex4.select_granularity(2048, 12288, 4096, 0.5) == (64, 64)
     assert apex4.select_granularity(8192, 28672, 8192, 0.5) == (64, 64)
     assert apex4.select_granularity(8192, 28672, 8192, 0.55) == (128, 128)
@@ -31,13 +31,15 @@ def test_prefill_picks_g64_at_half_speed():
 
 
 def test_prefill_tighter_budgets_coarsen():
-    # M = 8192: g=128 1627/2361 = 0.689 qualifies at 0.68; at 0.70 and 0.72
-    # mixed (1729/2361 = 0.732) is the finest that does; at 0.75 only g=256
-    # (1791/2361 = 0.759) and coarser; at 0.8 only g=K
+    # M = 8192: g=128 1625/2358 = 0.689 qualifies at 0.68; at 0.70 and 0.71
+    # mixed (1689/2358 = 0.716) is the finest that does; at 0.72 and 0.74
+    # only g=256 (1761/2358 = 0.747) and coarser; from 0.75 only g=K
     assert apex4.select_granularity(8192, 28672, 8192, 0.68) == (128, 128)
     assert apex4.select_granularity(8192, 28672, 8192, 0.70) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (128, 8192)
-    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.71) == (128, 8192)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.72) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.74) == (256, 256)
+    assert apex4.select_granularity(8192, 28672, 8192, 0.75) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.77) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 0.80) == (8192, 8192)
     assert apex4.select_granularity(8192, 28672, 8192, 1.0) == (8192, 8192)
@@ -46,7 +48,7 @@ def test_prefill_tighter_budgets_coarsen():
 def test_decode_picks_a_streaming_mode():
     # M = 1, N = 28672, K = 8192: the streaming kernels read ~118-125 MB at
     # ~5.2 TB/s (mixed mode fastest, 22.4 us; g=128 23.6 us, 0.95 of it); g=32
-    # and g=64 run on 256-row tiles (~240 and ~115 us)
+    # and g=64 run on 256-row tiles (~225 and ~118 us)
     assert apex4.select_granularity(1, 28672, 8192, 0.75) == (128, 128)
     assert apex4.select_granularity(1, 28672, 8192, 0.96) == (128, 8192)
     for M in (1, 4, 16, 64):
@@ -56,11 +58,11 @@ def test_decode_picks_a_streaming_mode():
 
 
 def test_decode_fine_groups_only_on_a_tiny_budget():
-    # accepting 11x slower than the fastest mode admits g=32 on 256-row tiles
-    # (0.093); 5x slower g=64 (0.19)
+    # accepting 10x slower than the fastest mode admits g=32 on 256-row tiles
+    # (0.100); 5x slower g=64 (0.19)
     assert apex4.select_granularity(1, 28672, 8192, 0.05) == (32, 32)
     assert apex4.select_granularity(1, 28672, 8192, 0.09) == (32, 32)
-    assert apex4.select_granularity(1, 28672, 8192, 0.10) == (64, 64)
+    assert apex4.select_granularity(1, 28672, 8192, 0.11) == (64, 64)
 
 
 def test_one_group_over_large_k_not_offered():
