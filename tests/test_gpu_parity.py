@@ -262,6 +262,19 @@ def test_gemm_debug_rows(dev, M, g):
     run_case(dev, x, w, g, g, rows=sample_rows(M, n=4), want_p=True, p_rows=(row0, step, count))
 
 
+@pytest.mark.parametrize("M", [300, 520])
+def test_gemm_debug_rows_step_major(dev, M):
+    """The same for the step-major tiled kernel, which runs mixed mode with
+    activation groups of 32 (per-channel weight scales): the kept rows' group
+    sums against the oracle."""
+    K = 1024
+    x, w = inputs.problem(M, 200, K, seed=9 + M, act="outlier")
+    row0 = M // 3
+    step = max(1, M // 5)
+    count = (M - 1 - row0) // step + 1
+    run_case(dev, x, w, 32, K, rows=sample_rows(M, n=4), want_p=True, p_rows=(row0, step, count))
+
+
 @pytest.mark.parametrize("g", [32, 64, 128, 256, 1024])
 def test_gemm_unit_scales_integer_exact(dev, g):
     """Random packed codes (-8 included), all scales 1: Y is the exact integer matmul."""
